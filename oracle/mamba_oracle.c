@@ -1,0 +1,135 @@
+/*
+ * mamba_oracle.c -- plain fp64 CPU reference of Mamba's selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this file;
+ * only the test-suite, the smoke check and the benchmark's CPU-baseline leg use it.  It shares
+ * no code, header, table or constant with the GPU library.
+ *
+ * What it computes (sources, by page title and section):
+ *  - "Mamba" (elemedex dex entry), section "How it works": the discrete SSM is the linear
+ *    recurrence h_t = Abar*h_{t-1} + Bbar*x_t with readout y_t = C*h_t, and Delta, B and C are
+ *    functions of the current token (selection).
+ *  - "State Spaces, Selectively -- Mamba" (papermap explainer), chapter 02 "The Discretized View":
+ *    a step size Delta turns h'(t) = A h(t) + B x(t) into the discrete recurrence, with Abar and
+ *    Bbar derived from (Delta, A, B); a large Delta lets the current token dominate the state.
+ *  - "Mamba remembers by forgetting, read closely" (interactiveml.org), the scalar equation:
+ *    zero-order hold with A = -1 gives h_t = exp(-Delta_t) h_{t-1} + (1 - exp(-Delta_t)) x_t,
+ *    starting from a zero state.
+ *  - The per-element rules that the pages leave open are taken as: Delta = softplus(raw + bias)
+ *    (bias added first, softplus only when requested), Abar = exp(Delta*A[d,n]),
+ *    Bbar*x = Delta*B[b,n,t]*u[b,d,t], readout after the update, an optional skip D[d]*u added
+ *    before the gate, and the output gate y*silu(z) ("Mamba" (visual-learn), "Simplifications and
+ *    limits": the block ends in an output gate; "Mamba" (elemedex) "How it works": a
+ *    multiplicative gate).
+ *
+ * The recurrence is evaluated strictly sequentially in t for every channel, in double precision,
+ * with no scan, blocking or reordering: the pages state that composing affine updates in any
+ * grouping reaches the same result ("Mamba remembers by forgetting", the composition equation),
+ * so the sequential loop is the plain definition.  OpenMP parallelism is over independent
+ * (batch, channel) pairs only; the t and n loops stay in order.
+ *
+ * Layouts (dense, row-major): u, delta, z, out: (batch, dim, seqlen); B, C: (batch, dstate,
+ * seqlen); A: (dim, dstate); D, delta_bias: (dim); last_state: (batch, dim, dstate).
+ * NULL for D, z, delta_bias or last_state means: no skip, no gate, zero bias, not written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(x) = log(1 + e^x), in the overflow-free form max(x,0) + log1p(e^-|x|). */
+static double sp(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+double ref_softplus_f64(double x) { return sp(x); }
+double ref_silu_f64(double z) { return silu(z); }
+
+void ref_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int ref_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* One token of the selective SSM for one channel: updates h[0..N-1] in place and returns y.
+ * x = u[b,d,t], draw = raw Delta, bn/cn = B[b,:,t]/C[b,:,t] with element stride bstride. */
+static double one_step(double* h, const double* Arow, int64_t N, double x, double draw, double bias,
+                       int softplus_flag, const double* Bp, const double* Cp, int64_t bstride,
+                       int has_D, double Dd, int has_z, double zz) {
+  double dt = draw + bias;
+  if (softplus_flag) dt = sp(dt);
+  double y = 0.0;
+  for (int64_t n = 0; n < N; ++n) {
+    double abar = exp(dt * Arow[n]);
+    double bx = dt * Bp[n * bstride] * x;
+    h[n] = abar * h[n] + bx;
+    y += Cp[n * bstride] * h[n];
+  }
+  if (has_D) y += Dd * x;
+  if (has_z) y *= silu(zz);
+  return y;
+}
+
+/* Whole-sequence forward from a zero state. */
+void ref_scan_fwd_f64(const double* u, const double* delta, const double* A, const double* B,
+                      const double* C, const double* D, const double* z, const double* delta_bias,
+                      int softplus_flag, int64_t batch, int64_t dim, int64_t dstate,
+                      int64_t seqlen, double* out, double* last_state) {
+  const int64_t nch = batch * dim;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t b = ch / dim, d = ch % dim;
+    double* h = (double*)calloc((size_t)dstate, sizeof(double));
+    const double bias = delta_bias ? delta_bias[d] : 0.0;
+    const double* Arow = A + d * dstate;
+    const int64_t row = (b * dim + d) * seqlen;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      out[row + t] = one_step(h, Arow, dstate, u[row + t], delta[row + t], bias, softplus_flag,
+                              B + b * dstate * seqlen + t, C + b * dstate * seqlen + t, seqlen,
+                              D != NULL, D ? D[d] : 0.0, z != NULL, z ? z[row + t] : 0.0);
+    }
+    if (last_state) memcpy(last_state + (b * dim + d) * dstate, h, (size_t)dstate * sizeof(double));
+    free(h);
+  }
+}
+
+/* One generation step: state (batch, dim, dstate) is read and written in place; u, delta, z, out
+ * are (batch, dim); B, C are (batch, dstate). */
+void ref_state_update_f64(double* state, const double* u, const double* delta, const double* A,
+                          const double* B, const double* C, const double* D, const double* z,
+                          const double* delta_bias, int softplus_flag, int64_t batch, int64_t dim,
+                          int64_t dstate, double* out) {
+  const int64_t nch = batch * dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t b = ch / dim, d = ch % dim;
+    out[ch] = one_step(state + ch * dstate, A + d * dstate, dstate, u[ch], delta[ch],
+                       delta_bias ? delta_bias[d] : 0.0, softplus_flag, B + b * dstate,
+                       C + b * dstate, 1, D != NULL, D ? D[d] : 0.0, z != NULL, z ? z[ch] : 0.0);
+  }
+}
+
+/* Scalar affine recurrence h_t = a_t*h_{t-1} + b_t from h_{-1} = h0 (the update
+ * "multiply by a, then add b" of "Mamba" (visual-learn), "Training without stepping token by
+ * token"). Writes every h_t. */
+void ref_affine_scan_f64(const double* a, const double* b, int64_t n, double h0, double* h) {
+  double s = h0;
+  for (int64_t t = 0; t < n; ++t) {
+    s = a[t] * s + b[t];
+    h[t] = s;
+  }
+}
