@@ -1,0 +1,299 @@
+"""Benchmark of the selective-scan forward on one MI355X.
+
+One step = one selective-scan forward (Delta/discretization/recurrence/readout/skip/gate) over
+the whole 2.8B-layer-shaped workload: batch 8, 5120 channels, 16 states, 2048 tokens, bf16
+u/Delta/z/B/C/out, fp32 A/D/bias/state, fp32 arithmetic -- 83,886,080 channel-steps.  Inputs are
+seeded synthetic data resident in HBM before timing starts.  The single-token state update of
+the generation workload (256 x 5120 x 16 fp32 states, bf16 tokens) is timed in the same run and
+reported in its own field.
+
+Prints one JSON line.  Roofline: the scan is bound by VALU issue on gfx950 (see the design doc for
+the derivation of the per-channel-step op count and the peak); the HBM figure the metric names
+is reported next to it.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "scan_fwd_2p8b_layer_counters.json")
+HBM_PEAK_GBS = 8000.0
+# VALU peak of the chip in lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz (non-packed fp32;
+# one lane-op per lane-cycle; a transcendental counts 2 lane-ops, its issue cost on gfx950).
+ALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# Algorithmic lane-ops per channel-step at N = 16:
+#   per state: Delta*A' (1), exp2 (2), Delta*u*B (1), h fma (1), C*h fma (1)  -> 6 x 16 = 96
+#   per channel-step: bias add 1, softplus (mul 1, exp2 2, log 2, mul 1, max/add 2) 9,
+#   Delta*u 1, skip fma 1, silu (mul 1, exp2 2, add 1, rcp 2, mul 1) 7, gate mul 1  -> 19
+ALU_OPS_PER_CHANNEL_STEP = 96 + 19
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_47_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def scan_alg_bytes(batch, dim, L, N, s_in, s_out):
+    """Bytes the method must move: u, Delta, z read and out written per channel-step; B and C
+    per (sequence, token); last_state written; A, D, bias read."""
+    return (batch * L * dim * (3 * s_in + s_out) + batch * L * 2 * N * s_in + batch * dim * N * 4
+            + dim * N * 4 + 2 * dim * 4)
+
+
+def step_alg_bytes(batch, dim, N, s_in, s_out):
+    """State read + write, u/Delta/z read and out written per channel; B, C per sequence."""
+    return batch * dim * (2 * N * 4 + 3 * s_in + s_out) + batch * 2 * N * s_in + dim * (N + 2) * 4
+
+
+def parse_counters(fetch_csv, write_csv, out_json, scan_bytes_alg):
+    """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into per-launch HBM
+    bytes for the scan kernel, scaled by the same counters on a plain device copy of 1 GiB."""
+    import csv
+
+    def read(path, counter):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r.get("Kernel_Name", "")
+                per.setdefault(name, []).append(float(r["Counter_Value"]))
+        return per
+
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = read(path, counter)
+        scan = [v for k, vs in per.items() if "scan_kernel" in k for v in vs]
+        other = [(max(vs), k) for k, vs in per.items() if "scan_kernel" not in k]
+        copy = per[max(other)[1]] if other else []
+        if not scan or not copy:
+            raise SystemExit(f"{counter}: scan or copy kernel not found in {path}: {list(per)}")
+        scan_kib = sorted(scan)[len(scan) // 2]
+        copy_kib = sorted(copy)[len(copy) // 2]
+        factor = (1 << 30) / (copy_kib * 1024.0)
+        res[counter] = dict(scan_kib_per_dispatch=scan_kib, copy_kib_per_dispatch=copy_kib,
+                            copy_bytes=1 << 30, scale=factor,
+                            scan_bytes_scaled=scan_kib * 1024.0 * factor)
+    total = res["FETCH_SIZE"]["scan_bytes_scaled"] + res["WRITE_SIZE"]["scan_bytes_scaled"]
+    doc = dict(kernel="scan_kernel<bf16, main> (2p8b_layer workload)",
+               source_hash=kernel_source_hash(), counters=res, traffic_bytes_per_launch=total,
+               algorithmic_bytes_per_launch=scan_bytes_alg,
+               traffic_over_algorithmic=total / scan_bytes_alg)
+    with open(out_json, "w") as f:
+        json.dump(doc, f, indent=1)
+    print(json.dumps(doc, indent=1))
+
+
+def cpu_baseline(x, w, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample: the first k channels (whole sequences)
+    of the same workload, k chosen for about `target_s` seconds of host time."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    L = w.seqlen
+
+    def run(k):
+        bsel = np.arange(k) // w.dim
+        dsel = np.arange(k) % w.dim
+        assert (bsel == 0).all()
+        u = x["u"][0, :k][None]
+        dl = x["delta"][0, :k][None]
+        z = x["z"][0, :k][None]
+        t0 = time.perf_counter()
+        oracle.scan_ref(u, dl, x["A"][dsel], x["B"][:1], x["C"][:1], x["D"][dsel], z,
+                        x["delta_bias"][dsel], True)
+        return time.perf_counter() - t0
+
+    k0 = max(threads, 16)
+    dt0 = run(k0)
+    k = int(min(w.dim, max(k0, k0 * target_s / max(dt0, 1e-3))))
+    k = max(threads, (k // threads) * threads)
+    dt = run(k)
+    return dict(value=k * L / dt, unit="channel-steps/s", cores=min(threads, k), kind="oracle",
+                sample=f"{k} channels x {L} tokens of sequence 0 of the {w.name} workload "
+                       f"({k * L} channel-steps, {dt:.1f} s, fp64, OpenMP over channels)")
+
+
+def bench_state_update(steps, torch, binding, synth, dev):
+    w = synth.WORKLOADS["gen_step"]
+    x = synth.step_inputs(w, steps=steps)
+    st = torch.from_numpy(x["state0"]).to(dev)
+    A, D, bias = (torch.from_numpy(x[k]).to(dev) for k in ("A", "D", "delta_bias"))
+    tok = {k: torch.from_numpy(x[k]).to(dev).to(torch.bfloat16)
+           for k in ("u", "delta", "z", "B", "C")}
+    del x
+    out = torch.empty((w.batch, w.dim), dtype=torch.bfloat16, device=dev)
+    for s in range(min(10, steps)):
+        binding.mamba_state_update(st, tok["u"][s], tok["delta"][s], A, tok["B"][s], tok["C"][s],
+                                   D, tok["z"][s], bias, True, out=out)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(steps):
+        binding.mamba_state_update(st, tok["u"][s], tok["delta"][s], A, tok["B"][s], tok["C"][s],
+                                   D, tok["z"][s], bias, True, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per = ms / steps
+    nbytes = step_alg_bytes(w.batch, w.dim, w.dstate, 2, 2)
+    return dict(workload="gen_step", batch=w.batch, dim=w.dim, dstate=w.dstate, steps=steps,
+                us_per_step=per * 1e3, channel_steps_per_s=w.batch * w.dim / (per * 1e-3),
+                effective_GBps=nbytes / (per * 1e-3) / 1e9,
+                effective_frac_of_hbm_peak=nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                note="state (80 MiB) is updated in place every step and fits the 256 MB "
+                     "Infinity Cache: effective bandwidth, wall time over back-to-back launches")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="2p8b_layer")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-step", action="store_true", help="skip the state-update timing")
+    ap.add_argument("--step-steps", type=int, default=1000)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+
+    from selective_state_space_47_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    bf = w.io_dtype == "bf16"
+    s_io = 2 if bf else 4
+    alg_bytes = scan_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s_io, s_io)
+
+    if args.parse_counters:
+        parse_counters(args.parse_counters[0], args.parse_counters[1], PROFILE_COUNTERS, alg_bytes)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the selective scan on a single "
+              "MI355X (channels are independent; see DESIGN.md for how the path would shard). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from selective_state_space_47_amd import _build, binding
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = synth.scan_inputs(w)
+    io = torch.bfloat16 if bf else torch.float32
+    t = {}
+    for k, v in x.items():
+        tt = torch.from_numpy(v).to(dev)
+        t[k] = tt.to(io) if k in ("u", "delta", "z", "B", "C") else tt
+    out = torch.empty((w.batch, w.dim, w.seqlen), dtype=io, device=dev)
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    ws_bytes = binding.mamba_scan_workspace_bytes(w.batch, w.dim, w.seqlen, io)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                               t["delta_bias"], True, return_last_state=True, out=out,
+                               last_state=last, workspace=ws if ws_bytes else None)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms.sort()
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    chsteps = w.batch * w.dim * w.seqlen
+    value = args.steps * chsteps / wall
+    ok = bool(torch.isfinite(out.float()).all().item())
+
+    if args.calib_copy:
+        # plain streaming copy of a known size for counter calibration: reads 1 GiB, writes
+        # 1 GiB (an elementwise multiply by one; the largest non-scan dispatch of this run)
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+
+    alu_achieved = chsteps * ALU_OPS_PER_CHANNEL_STEP / (kern_avg * 1e-3)
+    hbm_achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        with open(PROFILE_COUNTERS) as f:
+            prof = json.load(f)
+        if prof.get("source_hash") == kernel_source_hash() and args.workload == "2p8b_layer":
+            traffic = prof["traffic_bytes_per_launch"]
+
+    rec = {
+        "metric": "selective-scan B·D·L channel-steps/s + achieved HBM GB/s "
+                  "(% of peak), 1 MI355X",
+        "value": value,
+        "unit": "channel-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "seqlen": w.seqlen, "io_dtype": w.io_dtype, "state_dtype": "f32",
+                   "softplus": True, "delta_bias": True, "D": True, "z_gate": True,
+                   "channel_steps": chsteps, "chunks": 1 if ws_bytes == 0 else "multi"},
+        "roofline": {"bound": "alu", "achieved": alu_achieved / 1e12,
+                     "peak": ALU_PEAK_LANE_OPS / 1e12, "unit": "T lane-op/s",
+                     "frac": alu_achieved / ALU_PEAK_LANE_OPS, "traffic": traffic,
+                     "kernel": "scan_kernel<bf16, main>",
+                     "ops_per_channel_step": ALU_OPS_PER_CHANNEL_STEP},
+        "hbm": {"achieved_GBps": hbm_achieved, "peak_GBps": HBM_PEAK_GBS,
+                "frac": hbm_achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg_bytes,
+                "bytes_per_channel_step": alg_bytes / chsteps},
+        "kernel_us": {"mean": kern_avg * 1e3, "p10": kern_ms[len(kern_ms) // 10] * 1e3,
+                      "median": kern_ms[len(kern_ms) // 2] * 1e3,
+                      "p90": kern_ms[(len(kern_ms) * 9) // 10] * 1e3},
+        "outputs_finite": ok,
+    }
+    if not args.no_step:
+        del t, out
+        torch.cuda.empty_cache()
+        rec["state_update"] = bench_state_update(args.step_steps, torch, binding, synth, dev)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

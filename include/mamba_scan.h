@@ -1,0 +1,128 @@
+/*
+ * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Two operations, both from the discrete selective state-space model:
+ *
+ *   mamba_scan_fwd      the whole-sequence forward ("scan") over known tokens;
+ *   mamba_state_update  one generation step for one new token per sequence.
+ *
+ * The model (sources by page title and section):
+ *   - "Mamba" (elemedex dex entry), "How it works": h_t = Abar*h_{t-1} + Bbar*x_t, y_t = C*h_t,
+ *     with Delta, B and C functions of the current token.
+ *   - "State Spaces, Selectively -- Mamba" (papermap explainer), chapter 02 "The Discretized
+ *     View": the step size Delta discretizes the continuous SSM; Abar and Bbar derive from
+ *     (Delta, A, B); the hardware-aware scan never materializes the expanded state in HBM, and
+ *     generation is a pure recurrence with O(1) work per token.
+ *   - "Mamba" (visual-learn), "Training without stepping token by token": during training the
+ *     whole sequence is known and the affine updates are combined as a parallel scan; during
+ *     generation the state is updated one token at a time.
+ *   - Per element (the rules the pages leave open, fixed here):
+ *       delta  = softplus(delta_raw + delta_bias[d])   (bias optional; softplus if flag != 0)
+ *       Abar_n = exp(delta * A[d,n])
+ *       Bbar_n * x = delta * B[b,n,t] * u[b,d,t]
+ *       h_n    = Abar_n * h_n + Bbar_n * x            (h starts at 0 for the scan)
+ *       y      = sum_n C[b,n,t] * h_n + D[d] * u      (D optional; readout after the update)
+ *       out    = y * silu(z[b,d,t])                   (z optional; silu(z) = z / (1 + e^-z))
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (memory the caller allocated on the current HIP
+ *     device).  The caller owns every buffer; the library allocates nothing, keeps no pointer
+ *     after returning and holds no global state.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the default stream)
+ *     and runs asynchronously.  Buffers must stay valid until the stream reaches the work.
+ *     The library never synchronizes; device faults surface at the caller's synchronization.
+ *   - Arguments are validated on the host before anything is launched.  On any error nothing is
+ *     launched and nothing is written; the return value is a negative MAMBA_ERR_* code.
+ *   - `out` must not alias any input; `state` must not alias `out`.
+ *   - Calls on different streams with different output and workspace buffers are thread-safe.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA_SCAN_ABI_VERSION 1
+
+enum mamba_status {
+  MAMBA_OK = 0,
+  MAMBA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MAMBA_ERR_SHAPE = -2,       /* a dimension is <= 0, too large, or chunk_len is invalid */
+  MAMBA_ERR_DTYPE = -3,       /* io_dtype is not one of enum mamba_dtype */
+  MAMBA_ERR_UNSUPPORTED = -4, /* dstate != 16 */
+  MAMBA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size */
+  MAMBA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than mamba_scan_workspace_bytes() */
+  MAMBA_ERR_HIP = -7          /* the HIP runtime rejected a launch */
+};
+
+/* Storage type of u, delta, z, B, C and out.  A, D, delta_bias, last_state and state are
+ * always fp32.  Arithmetic is always fp32; bf16 outputs are rounded to nearest, ties to even. */
+enum mamba_dtype { MAMBA_F32 = 0, MAMBA_BF16 = 1 };
+
+typedef struct mamba_dims {
+  int64_t batch;     /* number of sequences, >= 1 */
+  int64_t dim;       /* channels D, >= 1 */
+  int64_t dstate;    /* state size N; must be 16 */
+  int64_t seqlen;    /* tokens L, >= 1 (must be 1 for mamba_state_update) */
+  int32_t io_dtype;  /* enum mamba_dtype */
+  int32_t chunk_len; /* scan only: 0 = chosen by the library; otherwise the sequence is split into
+                        chunks of this many tokens (a positive multiple of 16) whose carries are
+                        combined with the affine composition rule.  Results agree up to fp32
+                        rounding for every chunk length. */
+} mamba_dims;
+
+/* Bytes of device workspace mamba_scan_fwd needs for these dims (0 when the sequence is processed
+ * as a single chunk).  Returns 0 as well for invalid dims (mamba_scan_fwd reports the error). */
+size_t mamba_scan_workspace_bytes(const mamba_dims* dims);
+
+/*
+ * Selective-scan forward from a zero state over `seqlen` tokens.
+ *
+ *   u, delta, z, out : (batch, dim, seqlen), seqlen innermost, io_dtype
+ *   B, C             : (batch, dstate, seqlen), io_dtype; shared by all channels of a sequence
+ *   A                : (dim, dstate) fp32
+ *   D, delta_bias    : (dim) fp32
+ *   last_state       : (batch, dim, dstate) fp32; receives h after the last token
+ *   workspace        : device scratch of at least mamba_scan_workspace_bytes(dims) bytes
+ *                      (may be NULL when that is 0); contents on entry are ignored
+ *
+ * NULL allowed for D (no skip), z (no gate), delta_bias (zero bias), last_state (not written).
+ * softplus_flag != 0 applies softplus to delta_raw + bias.
+ */
+int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                   void* out, float* last_state, const mamba_dims* dims, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * One generation step for `batch` sequences: the state is read and updated in place and one
+ * output per channel is written.
+ *
+ *   state            : (batch, dim, dstate) fp32, updated in place
+ *   u, delta, z, out : (batch, dim), io_dtype
+ *   B, C             : (batch, dstate), io_dtype
+ *   A, D, delta_bias : as for mamba_scan_fwd
+ *
+ * dims->seqlen must be 1; dims->chunk_len is ignored.  NULL allowed for D, z, delta_bias.
+ */
+int mamba_state_update(float* state, const void* u, const void* delta, const float* A,
+                       const void* B, const void* C, const float* D, const void* z,
+                       const float* delta_bias, int softplus_flag, void* out,
+                       const mamba_dims* dims, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* mamba_status_string(int status);
+
+/* MAMBA_SCAN_ABI_VERSION of the built library. */
+int mamba_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

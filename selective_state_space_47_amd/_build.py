@@ -1,0 +1,50 @@
+"""Build the gfx950 HIP library in-tree (hipcc, no JIT cache)."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_DIR = os.path.join(PKG, "_lib")
+LIB_PATH = os.path.join(LIB_DIR, "libmamba_scan.so")
+SOURCES = [os.path.join(CSRC, "mamba_scan.hip")]
+
+HIPCC_FLAGS = [
+    "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 VALU ops (v_pk_*_f32) stay disabled on this target
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into selective_state_space_47_amd/_lib/libmamba_scan.so."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp] + SOURCES
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    if verbose and res.stderr:
+        print(res.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def emit_asm(out_path: str) -> None:
+    """Write the gfx950 assembly of the library (for inspection of the generated code)."""
+    cmd = [hipcc()] + [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")] + [
+        "--cuda-device-only", "-S", "-I", INCLUDE, "-o", out_path] + SOURCES
+    subprocess.run(cmd, check=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,199 @@
+"""Thin ctypes binding over the C ABI in include/mamba_scan.h.
+
+Argument marshalling only: checks dtypes, shapes and devices, allocates outputs and workspace with
+torch, passes raw device pointers and torch's current HIP stream to the library.  Every step of
+the computation runs in the library's kernels.  There is no fallback: if the native library is
+missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import _build
+
+MAMBA_F32 = 0
+MAMBA_BF16 = 1
+DSTATE = 16
+
+_lock = threading.Lock()
+_LIB = None
+
+
+class mamba_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int32)]
+
+
+EXPORTS = ("mamba_scan_fwd", "mamba_state_update", "mamba_scan_workspace_bytes",
+           "mamba_status_string", "mamba_abi_version")
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def lib():
+    """The loaded native library (raises RuntimeError if it has not been built)."""
+    global _LIB
+    with _lock:
+        if _LIB is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"native library {path} is missing: build it with "
+                    "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+            L = ctypes.CDLL(path)
+            vp, fp = ctypes.c_void_p, ctypes.c_void_p
+            dp = ctypes.POINTER(mamba_dims)
+            L.mamba_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp, fp, dp,
+                                         vp, ctypes.c_size_t, vp]
+            L.mamba_scan_fwd.restype = ctypes.c_int
+            L.mamba_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp,
+                                             dp, vp]
+            L.mamba_state_update.restype = ctypes.c_int
+            L.mamba_scan_workspace_bytes.argtypes = [dp]
+            L.mamba_scan_workspace_bytes.restype = ctypes.c_size_t
+            L.mamba_status_string.argtypes = [ctypes.c_int]
+            L.mamba_status_string.restype = ctypes.c_char_p
+            L.mamba_abi_version.argtypes = []
+            L.mamba_abi_version.restype = ctypes.c_int
+            _LIB = L
+    return _LIB
+
+
+def mamba_status_string(status: int) -> str:
+    return lib().mamba_status_string(int(status)).decode()
+
+
+def mamba_abi_version() -> int:
+    return int(lib().mamba_abi_version())
+
+
+def _io_code(dtype) -> int:
+    if dtype == torch.float32:
+        return MAMBA_F32
+    if dtype == torch.bfloat16:
+        return MAMBA_BF16
+    raise ValueError(f"unsupported io dtype {dtype}; use float32 or bfloat16")
+
+
+def make_dims(batch, dim, seqlen, io_dtype, dstate=DSTATE, chunk_len=0) -> mamba_dims:
+    return mamba_dims(int(batch), int(dim), int(dstate), int(seqlen), int(io_dtype),
+                      int(chunk_len))
+
+
+def mamba_scan_workspace_bytes(batch, dim, seqlen, io_dtype=torch.float32, dstate=DSTATE,
+                               chunk_len=0) -> int:
+    code = io_dtype if isinstance(io_dtype, int) else _io_code(io_dtype)
+    dm = make_dims(batch, dim, seqlen, code, dstate, chunk_len)
+    return int(lib().mamba_scan_workspace_bytes(ctypes.byref(dm)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(status):
+    if status != 0:
+        raise ValueError(f"mamba library error {status}: {mamba_status_string(status)}")
+
+
+def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   return_last_state=False, chunk_len=0, out=None, last_state=None,
+                   workspace=None):
+    """Selective-scan forward (see mamba_scan_fwd in include/mamba_scan.h).
+
+    u, delta, z: (batch, dim, L); B, C: (batch, 16, L) -- all float32 or all bfloat16;
+    A: (dim, 16) float32; D, delta_bias: (dim,) float32.  Returns out, or (out, last_state).
+    """
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, L = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io = u.dtype
+    code = _io_code(io)
+    _check(u, "u", (batch, dim, L), io, dev)
+    _check(delta, "delta", (batch, dim, L), io, dev)
+    _check(z, "z", (batch, dim, L), io, dev)
+    _check(B, "B", (batch, DSTATE, L), io, dev)
+    _check(C, "C", (batch, DSTATE, L), io, dev)
+    _check(A, "A", (dim, DSTATE), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _check(out, "out", (batch, dim, L), io, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, DSTATE), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, dim, DSTATE), torch.float32, dev)
+    dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+    L_ = lib()
+    ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = L_.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                           _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
+                           _ptr(last_state), ctypes.byref(dm), ws_ptr, ws_len, stream)
+    _raise(st)
+    return (out, last_state) if return_last_state else out
+
+
+def mamba_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=False, out=None):
+    """One generation step (see mamba_state_update in include/mamba_scan.h).
+
+    state: (batch, dim, 16) float32, updated in place; u, delta, z: (batch, dim);
+    B, C: (batch, 16); A: (dim, 16) float32; D, delta_bias: (dim,) float32.  Returns out.
+    """
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, 16)")
+    batch, dim, _ = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io = u.dtype
+    code = _io_code(io)
+    _check(state, "state", (batch, dim, DSTATE), torch.float32, dev)
+    _check(u, "u", (batch, dim), io, dev)
+    _check(delta, "delta", (batch, dim), io, dev)
+    _check(z, "z", (batch, dim), io, dev)
+    _check(B, "B", (batch, DSTATE), io, dev)
+    _check(C, "C", (batch, DSTATE), io, dev)
+    _check(A, "A", (dim, DSTATE), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=io, device=dev)
+    _check(out, "out", (batch, dim), io, dev)
+    dm = make_dims(batch, dim, 1, code, DSTATE, 0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = lib().mamba_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                  _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                                  _ptr(out), ctypes.byref(dm), stream)
+    _raise(st)
+    return out
