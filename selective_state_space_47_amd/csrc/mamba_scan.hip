@@ -37,41 +37,165 @@
 namespace {
 
 constexpr int kN = 16;                 // state size (fixed)
-constexpr int kT = 16;                 // tokens per tile
+constexpr int kTT = 64;                // tokens per tile (global loads, B/C staging)
+constexpr int kTS = 16;                // tokens per sub-tile (recurrence, readout reduction)
+constexpr int kSub = kTT / kTS;
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kChW = 8;                // channels per wave
 constexpr int kChWG = kWaves * kChW;   // channels per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kYStride = 20;           // floats per lane slot in the partial-readout buffer
+constexpr int kYStride = 20;           // floats per lane slot of the partial-readout buffer
+constexpr int kChunkAlign = 16;        // chunk lengths are multiples of this
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTargetWG = 1280;        // 5 workgroups of 4 waves per CU on 256 CUs
 
-// ------------------------------------------------------------------ element conversion
+// ------------------------------------------------------------------ element access
+//
+// Tokens are handled in pairs (t, t+1) with t even.  Raw pairs stay in registers between the
+// prefetch and their use: a uint32 holding two bf16, or a float2.
 
-__device__ __forceinline__ float ld_f32(const float* p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float ld_f32(const uint16_t* p, int64_t i) {
-  return __uint_as_float((uint32_t)p[i] << 16);
+template <typename Tin> struct RawPair;
+template <> struct RawPair<uint16_t> { using T = uint32_t; };
+template <> struct RawPair<float> { using T = float2; };
+
+__device__ __forceinline__ float2 unpack(uint32_t w) {
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
+__device__ __forceinline__ float2 unpack(float2 v) { return v; }
+__device__ __forceinline__ float unpack1(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float unpack1(float v) { return v; }
+
+template <bool kVec>
+__device__ __forceinline__ uint32_t load_pair(const uint16_t* p, int64_t i, bool ok0, bool ok1) {
+  if (kVec) return ok0 ? *reinterpret_cast<const uint32_t*>(p + i) : 0u;
+  uint32_t lo = ok0 ? p[i] : 0u, hi = ok1 ? p[i + 1] : 0u;
+  return lo | (hi << 16);
+}
+template <bool kVec>
+__device__ __forceinline__ float2 load_pair(const float* p, int64_t i, bool ok0, bool ok1) {
+  if (kVec) return ok0 ? *reinterpret_cast<const float2*>(p + i) : make_float2(0.f, 0.f);
+  return make_float2(ok0 ? p[i] : 0.f, ok1 ? p[i + 1] : 0.f);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> two bf16 in one dword with v_cvt_pk_bf16_f32 (round to nearest, ties to even)
+__device__ __forceinline__ uint32_t pack_bf16(float2 v) {
+  const f32x2_t f = {v.x, v.y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// single-element access (state-update kernel)
+__device__ __forceinline__ float ld_f32(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_f32(const uint16_t* p, int64_t i) { return unpack1(p[i]); }
 __device__ __forceinline__ void st_out(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) {
-  __bf16 b = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest, ties to even
-  p[i] = __builtin_bit_cast(uint16_t, b);
+  p[i] = (uint16_t)(pack_bf16(make_float2(v, 0.f)) & 0xffffu);
+}
+
+template <bool kVec>
+__device__ __forceinline__ void store_pair(uint16_t* p, int64_t i, float2 v, bool ok0, bool ok1) {
+  const uint32_t w = pack_bf16(v);
+  if (kVec) {
+    if (ok0) *reinterpret_cast<uint32_t*>(p + i) = w;
+  } else {
+    if (ok0) p[i] = (uint16_t)(w & 0xffffu);
+    if (ok1) p[i + 1] = (uint16_t)(w >> 16);
+  }
+}
+template <bool kVec>
+__device__ __forceinline__ void store_pair(float* p, int64_t i, float2 v, bool ok0, bool ok1) {
+  if (kVec) {
+    if (ok0) *reinterpret_cast<float2*>(p + i) = v;
+  } else {
+    if (ok0) p[i] = v.x;
+    if (ok1) p[i + 1] = v.y;
+  }
+}
+
+// Eight consecutive B or C values of one row (tokens t..t+7) for the LDS staging, kept raw in
+// registers until they are written to LDS.
+template <typename Tin> struct Raw8;
+template <> struct Raw8<uint16_t> { uint4 v; };
+template <> struct Raw8<float> { float4 a, b; };
+
+template <bool kVec>
+__device__ __forceinline__ Raw8<uint16_t> load8(const uint16_t* p, int64_t i, int64_t t,
+                                                int64_t t_end) {
+  Raw8<uint16_t> r;
+  if (kVec) {
+    r.v = (t < t_end) ? *reinterpret_cast<const uint4*>(p + i) : make_uint4(0, 0, 0, 0);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = (t + 2 * k < t_end) ? p[i + 2 * k] : 0u;
+      const uint32_t hi = (t + 2 * k + 1 < t_end) ? p[i + 2 * k + 1] : 0u;
+      w[k] = lo | (hi << 16);
+    }
+    r.v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return r;
+}
+template <bool kVec>
+__device__ __forceinline__ Raw8<float> load8(const float* p, int64_t i, int64_t t,
+                                             int64_t t_end) {
+  Raw8<float> r;
+  if (kVec) {
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.a = (t < t_end) ? *reinterpret_cast<const float4*>(p + i) : zero;
+    r.b = (t < t_end) ? *reinterpret_cast<const float4*>(p + i + 4) : zero;
+  } else {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (t + k < t_end) ? p[i + k] : 0.f;
+    r.a = make_float4(v[0], v[1], v[2], v[3]);
+    r.b = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  return r;
+}
+__device__ __forceinline__ float elem8(const Raw8<uint16_t>& r, int k) {
+  const uint32_t ws = (k >> 1) == 0 ? r.v.x : (k >> 1) == 1 ? r.v.y : (k >> 1) == 2 ? r.v.z : r.v.w;
+  return (k & 1) ? __uint_as_float(ws & 0xffff0000u) : __uint_as_float(ws << 16);
+}
+__device__ __forceinline__ float elem8(const Raw8<float>& r, int k) {
+  const float4 q = k < 4 ? r.a : r.b;
+  const int j = k & 3;
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
 
 // ------------------------------------------------------------------ scalar math
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// softplus(x) = max(x, 0) + log1p(exp(-|x|)); x itself above 20 (the dropped term is < 2.1e-9).
+// softplus(x) = max(x, 0) + log1p(e), e = exp(-|x|) in (0, 1].  log1p(e) is ln2*log2(u) for
+// u = 1 + e (rounded) plus a first-order correction for that rounding: the error
+// d = e - (u - 1) is exact (Sterbenz), and log(1+e) - log(u) = d/u + O(d^2) with 1/u taken as
+// 2 - u (|d| <= 2^-24, so the approximation of 1/u adds < 2^-26 absolute).  v_log_f32 is
+// relatively accurate near 1 on gfx950, so the result has relative error ~1e-6 or better over
+// the whole fp32 range; for large x, e underflows and the result is x.
 __device__ __forceinline__ float softplus_f32(float x) {
-  if (x > 20.f) return x;
-  float e = fast_exp2(-fabsf(x) * kLog2e);
-  return fmaxf(x, 0.f) + log1pf(e);
+  const float e = fast_exp2(-fabsf(x) * kLog2e);
+  const float u = 1.f + e;
+  const float d = e - (u - 1.f);
+  const float l = fmaf(__builtin_amdgcn_logf(u), kLn2, d * (2.f - u));
+  return fmaxf(x, 0.f) + l;
 }
 
 // silu(z) = z / (1 + exp(-z)).
 __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-z * kLog2e));
+}
+
+// Keeps the compiler from moving LDS accesses across this point.  Within one wavefront the
+// hardware executes LDS instructions in issue order, so this orders cross-lane exchanges
+// through LDS inside a wave.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ------------------------------------------------------------------ scan
@@ -97,27 +221,34 @@ struct ScanArgs {
 };
 
 struct __align__(16) ScanSmem {
-  float4 bc[2][kT][8];                 // (B_2g, B_2g+1, C_2g, C_2g+1) per token and lane group
-  float2 dd[kWaves][kT][kChW];         // (Delta, Delta*u) per token and channel
-  float y[kWaves][kChW * 8][kYStride]; // partial readouts per lane slot and token
+  float4 bc[kTT][8];                     // (B_2g, B_2g+1, C_2g, C_2g+1) per token and lane group
+  float2 dd[kWaves][kTS][kChW];          // (Delta, Delta*u) per token and channel
+  float y[kWaves][kChW * 8][kYStride];   // partial readouts per lane and token
 };
 
-// kMain = true: full forward of one chunk (carry-in, readout, epilogue, last_state).
+// One workgroup: 32 channels of one sequence over one chunk of tokens.
+//   lane = 8*c + g: channel c of the wave; g is the state group (states 2g, 2g+1) in the
+//   recurrence, and the token pair (2g, 2g+1 of each 16-token sub-tile) in the element-wise
+//   prologue/epilogue.
+// kMain = true: full forward of the chunk (carry-in, readout, epilogue, last_state).
 // kMain = false: chunk summary (local final state from zero and sum of Delta), no output.
-template <typename Tin, bool kMain>
-__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
+// kVec: seqlen % 8 == 0 and 16-byte aligned tensors -> vector loads and stores.
+template <typename Tin, bool kMain, bool kVec>
+__global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
+  using Raw = typename RawPair<Tin>::T;
   __shared__ ScanSmem sm;
   const Tin* __restrict__ U = static_cast<const Tin*>(p.u);
   const Tin* __restrict__ DL = static_cast<const Tin*>(p.delta);
   const Tin* __restrict__ Bm = static_cast<const Tin*>(p.B);
   const Tin* __restrict__ Cm = static_cast<const Tin*>(p.C);
   const Tin* __restrict__ Z = static_cast<const Tin*>(p.z);
+  const bool has_z = kMain && Z != nullptr;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int c = lane >> 3;  // channel within the wave (scan, prologue and epilogue)
-  const int g = lane & 7;   // state group (scan) / token pair (prologue, epilogue)
+  const int c = lane >> 3;
+  const int g = lane & 7;
 
   const int64_t nwg_ch = (int64_t)p.batch * p.dblocks;
   const int64_t k = blockIdx.x / nwg_ch;          // chunk
@@ -149,81 +280,103 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
     }
   }
 
-  // B/C staging assignment: thread -> (row r of the 32 B/C rows, token pair q)
+  // B/C staging assignment: thread -> (row r of the 32 B/C rows, 8-token segment q)
   const int sr = tid >> 3;
   const int sq = tid & 7;
   const int sn = sr & 15;
-  const Tin* __restrict__ BCsrc = (sr < 16 ? Bm : Cm) + (b * kN + sn) * p.L;
+  const Tin* __restrict__ BCrow = (sr < 16 ? Bm : Cm) + (b * kN + sn) * p.L;
   const int sslot = (sr < 16 ? 0 : 2) + (sn & 1);
   const int sg = sn >> 1;
 
-  float dsum = 0.f;  // summary: sum of Delta over this lane's tokens
-  int buf = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
-    // ---- stage B and C for this tile (fp32), shared by the workgroup
+  // ---- raw registers, prefetched one tile ahead: sub-tile s of the next tile is loaded as soon
+  // as sub-tile s of the current tile has consumed its registers (no copies), B/C right after
+  // they are staged in LDS.
+  Raw ru[kSub], rd[kSub], rz[kSub];
+  Raw8<Tin> rbc;
+  auto load_sub = [&](int64_t t0, int s) {
+    const int64_t t = t0 + kTS * s + 2 * g;
+    const bool ok0 = dvalid && t < t_end, ok1 = dvalid && t + 1 < t_end;
+    ru[s] = load_pair<kVec>(U, row + t, ok0, ok1);
+    rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
+    if (has_z) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
+  };
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int tl = 2 * sq + e;
-      const int64_t t = t0 + tl;
-      const float v = (t < t_end) ? ld_f32(BCsrc, t) : 0.f;
-      reinterpret_cast<float*>(&sm.bc[buf][tl][sg])[sslot] = v;
-    }
-    // ---- prologue: Delta and Delta*u per (channel, token), kept u and z for the epilogue
-    float uv[2], zv[2];
+  for (int s = 0; s < kSub; ++s) load_sub(t_begin, s);
+  rbc = load8<kVec>(BCrow, t_begin + 8 * sq, t_begin + 8 * sq, t_end);
+
+  float dsum = 0.f;  // summary kernel: sum of Delta over this lane's tokens
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
+    const int64_t tn = t0 + kTT;      // next tile
+    const bool more = tn < t_end;
+    __syncthreads();  // every wave is done reading the previous tile's B/C
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int tl = 2 * g + e;
-      const int64_t t = t0 + tl;
-      float dl = 0.f, du = 0.f;
-      uv[e] = 0.f;
-      zv[e] = 0.f;
-      if (dvalid && t < t_end) {
-        const float x = ld_f32(U, row + t);
-        float v = ld_f32(DL, row + t) + bias;
-        if (p.softplus) v = softplus_f32(v);
-        dl = v;
-        du = v * x;
-        uv[e] = x;
-        if (kMain && Z) zv[e] = ld_f32(Z, row + t);
-      }
-      dsum += dl;
-      sm.dd[w][tl][c] = make_float2(dl, du);
-    }
+    for (int i = 0; i < 8; ++i)
+      reinterpret_cast<float*>(&sm.bc[8 * sq + i][sg])[sslot] = elem8(rbc, i);
+    if (more) rbc = load8<kVec>(BCrow, tn + 8 * sq, tn + 8 * sq, t_end);
     __syncthreads();
 
-    // ---- sequential recurrence over the tile for this lane's two states
-    float yp[kT];
 #pragma unroll
-    for (int tl = 0; tl < kT; ++tl) {
-      const float2 q = sm.dd[w][tl][c];
-      const float4 bc = sm.bc[buf][tl][g];
-      const float e0 = fast_exp2(q.x * a0);
-      const float e1 = fast_exp2(q.x * a1);
-      h0 = fmaf(e0, h0, q.y * bc.x);
-      h1 = fmaf(e1, h1, q.y * bc.y);
-      if (kMain) yp[tl] = fmaf(bc.w, h1, bc.z * h0);
-    }
-
-    if (kMain) {
-      float4* ydst = reinterpret_cast<float4*>(&sm.y[w][lane][0]);
-#pragma unroll
-      for (int i = 0; i < kT / 4; ++i) ydst[i] = make_float4(yp[4 * i], yp[4 * i + 1],
-                                                            yp[4 * i + 2], yp[4 * i + 3]);
-      __syncthreads();
-      // ---- epilogue: sum the 8 partial readouts, skip, gate, store
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int tl = 2 * g + e;
-        const int64_t t = t0 + tl;
-        float y = 0.f;
-#pragma unroll
-        for (int gg = 0; gg < 8; ++gg) y += sm.y[w][c * 8 + gg][tl];
-        y = fmaf(dskip, uv[e], y);
-        if (Z) y *= silu_f32(zv[e]);
-        if (dvalid && t < t_end) st_out(static_cast<Tin*>(p.out), row + t, y);
+    for (int s = 0; s < kSub; ++s) {
+      const int64_t tp = t0 + kTS * s + 2 * g;  // this lane's token pair (prologue/epilogue)
+      const bool ok0 = dvalid && tp < t_end, ok1 = dvalid && tp + 1 < t_end;
+      // ---- prologue: Delta = softplus(raw + bias), Delta*u for the lane's two tokens
+      const float2 x = unpack(ru[s]);
+      const float2 dr = unpack(rd[s]);
+      float2 zz = make_float2(0.f, 0.f);
+      if (has_z) zz = unpack(rz[s]);
+      if (more) load_sub(tn, s);
+      float dl0 = dr.x + bias, dl1 = dr.y + bias;
+      if (p.softplus) {
+        dl0 = softplus_f32(dl0);
+        dl1 = softplus_f32(dl1);
       }
+      if (!ok0) dl0 = 0.f;
+      if (!ok1) dl1 = 0.f;
+      if (!kMain) dsum += dl0 + dl1;
+      sm.dd[w][2 * g][c] = make_float2(dl0, dl0 * x.x);
+      sm.dd[w][2 * g + 1][c] = make_float2(dl1, dl1 * x.y);
+      wave_lds_fence();
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- sequential recurrence over the sub-tile for this lane's two states
+      float yp[kTS];
+#pragma unroll
+      for (int tl = 0; tl < kTS; ++tl) {
+        const float2 q = sm.dd[w][tl][c];
+        const float4 bc = sm.bc[kTS * s + tl][g];
+        const float e0 = fast_exp2(q.x * a0);
+        const float e1 = fast_exp2(q.x * a1);
+        h0 = fmaf(e0, h0, q.y * bc.x);
+        h1 = fmaf(e1, h1, q.y * bc.y);
+        if (kMain) yp[tl] = fmaf(bc.w, h1, bc.z * h0);
+        // bound how far the scheduler hoists LDS reads (register pressure)
+        if (tl % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kMain) {
+        float4* ydst = reinterpret_cast<float4*>(&sm.y[w][lane][0]);
+#pragma unroll
+        for (int i = 0; i < kTS / 4; ++i)
+          ydst[i] = make_float4(yp[4 * i], yp[4 * i + 1], yp[4 * i + 2], yp[4 * i + 3]);
+        wave_lds_fence();
+        // ---- epilogue: sum the 8 partial readouts of tokens (2g, 2g+1), skip, gate, store
+        float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int gg = 0; gg < 8; ++gg) {
+          const float2 v = *reinterpret_cast<const float2*>(&sm.y[w][c * 8 + gg][2 * g]);
+          y.x += v.x;
+          y.y += v.y;
+        }
+        y.x = fmaf(dskip, x.x, y.x);
+        y.y = fmaf(dskip, x.y, y.y);
+        if (has_z) {
+          y.x *= silu_f32(zz.x);
+          y.y *= silu_f32(zz.y);
+        }
+        store_pair<kVec>(static_cast<Tin*>(p.out), row + tp, y, ok0, ok1);
+      }
+      wave_lds_fence();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    buf ^= 1;
   }
 
   if (kMain) {
@@ -231,16 +384,18 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs p) {
       p.last_state[ch * kN + 2 * g] = h0;
       p.last_state[ch * kN + 2 * g + 1] = h1;
     }
-  } else if (dvalid) {
-    const int64_t nsum = p.nchunks - 1;
-    p.ws_H[(ch * nsum + k) * kN + 2 * g] = h0;
-    p.ws_H[(ch * nsum + k) * kN + 2 * g + 1] = h1;
+  } else {
     // sum of Delta over the chunk: reduce the 8 token-pair lanes of this channel, fixed order
     float s = dsum;
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
     s += __shfl_xor(s, 4);
-    if (g == 0) p.ws_S[ch * nsum + k] = s;
+    if (dvalid) {
+      const int64_t nsum = p.nchunks - 1;
+      p.ws_H[(ch * nsum + k) * kN + 2 * g] = h0;
+      p.ws_H[(ch * nsum + k) * kN + 2 * g + 1] = h1;
+      if (g == 0) p.ws_S[ch * nsum + k] = s;
+    }
   }
 }
 
@@ -326,7 +481,7 @@ int check_dims(const mamba_dims* dm, bool step) {
   if (dm->batch > lim || dm->dim > lim || dm->seqlen > lim) return MAMBA_ERR_SHAPE;
   if ((double)dm->batch * (double)dm->dim * (double)dm->seqlen > (double)lim)
     return MAMBA_ERR_SHAPE;
-  if (!step && (dm->chunk_len < 0 || dm->chunk_len % kT != 0)) return MAMBA_ERR_SHAPE;
+  if (!step && (dm->chunk_len < 0 || dm->chunk_len % kChunkAlign != 0)) return MAMBA_ERR_SHAPE;
   return MAMBA_OK;
 }
 
@@ -337,10 +492,10 @@ int make_plan(const mamba_dims* dm, Plan* pl) {
   int64_t cl = dm->chunk_len;
   if (cl == 0) {
     int64_t K = (kTargetWG + nwg_ch - 1) / nwg_ch;
-    const int64_t maxK = (L + kT - 1) / kT;
+    const int64_t maxK = (L + kChunkAlign - 1) / kChunkAlign;
     if (K > maxK) K = maxK;
     if (K < 1) K = 1;
-    cl = ((L + K - 1) / K + kT - 1) / kT * kT;
+    cl = ((L + K - 1) / K + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
   }
   pl->chunk_len = cl;
   pl->nchunks = (L + cl - 1) / cl;
@@ -397,15 +552,21 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t nwg_ch = dims->batch * pl.dblocks;
   const bool bf = dims->io_dtype == MAMBA_BF16;
+  const bool vec = dims->seqlen % 8 == 0 && aligned(u, 16) && aligned(delta, 16) &&
+                   aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
   if (pl.nchunks > 1) {
     dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
-    if (bf) hipLaunchKernelGGL((scan_kernel<uint16_t, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((scan_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
+    if (bf && vec) hipLaunchKernelGGL((scan_kernel<uint16_t, false, true>), grid, dim3(kThreads), 0, s, a);
+    else if (bf) hipLaunchKernelGGL((scan_kernel<uint16_t, false, false>), grid, dim3(kThreads), 0, s, a);
+    else if (vec) hipLaunchKernelGGL((scan_kernel<float, false, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((scan_kernel<float, false, false>), grid, dim3(kThreads), 0, s, a);
     if (launch_status() != MAMBA_OK) return MAMBA_ERR_HIP;
   }
   dim3 grid((unsigned)(nwg_ch * pl.nchunks));
-  if (bf) hipLaunchKernelGGL((scan_kernel<uint16_t, true>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((scan_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
+  if (bf && vec) hipLaunchKernelGGL((scan_kernel<uint16_t, true, true>), grid, dim3(kThreads), 0, s, a);
+  else if (bf) hipLaunchKernelGGL((scan_kernel<uint16_t, true, false>), grid, dim3(kThreads), 0, s, a);
+  else if (vec) hipLaunchKernelGGL((scan_kernel<float, true, true>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((scan_kernel<float, true, false>), grid, dim3(kThreads), 0, s, a);
   return launch_status();
 }
 
