@@ -44,7 +44,8 @@ constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kChW = 8;                // channels per wave
 constexpr int kChWG = kWaves * kChW;   // channels per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kYStride = 20;           // floats per lane slot of the partial-readout buffer
+constexpr int kYStride = 18;           // floats per lane slot of the partial-readout buffer
+                                       // (18: b64 writes and reads both bank-conflict free)
 constexpr int kChunkAlign = 16;        // chunk lengths are multiples of this
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -171,17 +172,18 @@ __device__ __forceinline__ float elem8(const Raw8<float>& r, int k) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // softplus(x) = max(x, 0) + log1p(e), e = exp(-|x|) in (0, 1].  log1p(e) is ln2*log2(u) for
-// u = 1 + e (rounded) plus a first-order correction for that rounding: the error
-// d = e - (u - 1) is exact (Sterbenz), and log(1+e) - log(u) = d/u + O(d^2) with 1/u taken as
-// 2 - u (|d| <= 2^-24, so the approximation of 1/u adds < 2^-26 absolute).  v_log_f32 is
-// relatively accurate near 1 on gfx950, so the result has relative error ~1e-6 or better over
-// the whole fp32 range; for large x, e underflows and the result is x.
+// u = 1 + e (rounded) plus the rounding error d = e - (u - 1), which is exact (Sterbenz) and
+// |d| <= 2^-24: log(1+e) = log(u) + d/u + O(d^2), and using d for d/u errs by at most
+// |d|(1 - 1/u) < 3e-8 absolute, relative to log1p(e) < 6e-8.  v_log_f32 is relatively accurate
+// near 1 on gfx950 (measured 1.1e-7), so the result is accurate to ~1e-6 relative over the
+// fp32 range (dominated by the rounding of -|x|*log2(e) for large |x|).  max(x, 0) is formed as
+// (x + |x|)/2; NaN propagates; for large x, e underflows and the result is x.
 __device__ __forceinline__ float softplus_f32(float x) {
   const float e = fast_exp2(-fabsf(x) * kLog2e);
   const float u = 1.f + e;
   const float d = e - (u - 1.f);
-  const float l = fmaf(__builtin_amdgcn_logf(u), kLn2, d * (2.f - u));
-  return fmaxf(x, 0.f) + l;
+  const float l = fmaf(__builtin_amdgcn_logf(u), kLn2, d);
+  return fmaf(0.5f, x + fabsf(x), l);
 }
 
 // silu(z) = z / (1 + exp(-z)).
@@ -293,12 +295,23 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   // they are staged in LDS.
   Raw ru[kSub], rd[kSub], rz[kSub];
   Raw8<Tin> rbc;
+  // Tokens past t_end are never loaded; the remainder test is uniform, so full sub-tiles (all
+  // but the last of a chunk) take the unguarded path.  Lanes of channels >= dim read a valid
+  // row (channel clamped to the block's first) and never store.
   auto load_sub = [&](int64_t t0, int s) {
-    const int64_t t = t0 + kTS * s + 2 * g;
-    const bool ok0 = dvalid && t < t_end, ok1 = dvalid && t + 1 < t_end;
-    ru[s] = load_pair<kVec>(U, row + t, ok0, ok1);
-    rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
-    if (has_z) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
+    const int64_t tb = t0 + kTS * s;
+    const int64_t rem = t_end - tb;          // uniform
+    const int64_t t = tb + 2 * g;
+    if (rem >= kTS) {
+      ru[s] = load_pair<kVec>(U, row + t, true, true);
+      rd[s] = load_pair<kVec>(DL, row + t, true, true);
+      if (has_z) rz[s] = load_pair<kVec>(Z, row + t, true, true);
+    } else {
+      const bool ok0 = 2 * g < rem, ok1 = 2 * g + 1 < rem;
+      ru[s] = load_pair<kVec>(U, row + t, ok0, ok1);
+      rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
+      if (has_z) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
+    }
   };
 #pragma unroll
   for (int s = 0; s < kSub; ++s) load_sub(t_begin, s);
@@ -317,8 +330,10 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
 
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
-      const int64_t tp = t0 + kTS * s + 2 * g;  // this lane's token pair (prologue/epilogue)
-      const bool ok0 = dvalid && tp < t_end, ok1 = dvalid && tp + 1 < t_end;
+      const int64_t tb = t0 + kTS * s;
+      const int64_t rem = t_end - tb;          // uniform
+      const int64_t tp = tb + 2 * g;           // this lane's token pair (prologue/epilogue)
+      const bool ok0 = 2 * g < rem, ok1 = 2 * g + 1 < rem;
       // ---- prologue: Delta = softplus(raw + bias), Delta*u for the lane's two tokens
       const float2 x = unpack(ru[s]);
       const float2 dr = unpack(rd[s]);
@@ -330,8 +345,10 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
         dl0 = softplus_f32(dl0);
         dl1 = softplus_f32(dl1);
       }
-      if (!ok0) dl0 = 0.f;
-      if (!ok1) dl1 = 0.f;
+      if (rem < kTS) {  // tokens past the end of the chunk leave the state unchanged
+        if (!ok0) dl0 = 0.f;
+        if (!ok1) dl1 = 0.f;
+      }
       if (!kMain) dsum += dl0 + dl1;
       sm.dd[w][2 * g][c] = make_float2(dl0, dl0 * x.x);
       sm.dd[w][2 * g + 1][c] = make_float2(dl1, dl1 * x.y);
@@ -352,11 +369,14 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
         // bound how far the scheduler hoists LDS reads (register pressure)
         if (tl % 8 == 7) __builtin_amdgcn_sched_barrier(0);
       }
+      // The state must be complete at the end of the sub-tile (its LDS inputs are overwritten
+      // next); without this the summary kernel, which only needs h after the loop, sinks the
+      // arithmetic past later sub-tiles and keeps every loaded value live.
+      asm volatile("" : "+v"(h0), "+v"(h1));
       if (kMain) {
-        float4* ydst = reinterpret_cast<float4*>(&sm.y[w][lane][0]);
+        float2* ydst = reinterpret_cast<float2*>(&sm.y[w][lane][0]);
 #pragma unroll
-        for (int i = 0; i < kTS / 4; ++i)
-          ydst[i] = make_float4(yp[4 * i], yp[4 * i + 1], yp[4 * i + 2], yp[4 * i + 3]);
+        for (int i = 0; i < kTS / 2; ++i) ydst[i] = make_float2(yp[2 * i], yp[2 * i + 1]);
         wave_lds_fence();
         // ---- epilogue: sum the 8 partial readouts of tokens (2g, 2g+1), skip, gate, store
         float2 y = make_float2(0.f, 0.f);
@@ -372,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
           y.x *= silu_f32(zz.x);
           y.y *= silu_f32(zz.y);
         }
-        store_pair<kVec>(static_cast<Tin*>(p.out), row + tp, y, ok0, ok1);
+        store_pair<kVec>(static_cast<Tin*>(p.out), row + tp, y, dvalid && ok0, dvalid && ok1);
       }
       wave_lds_fence();
       __builtin_amdgcn_sched_barrier(0);
