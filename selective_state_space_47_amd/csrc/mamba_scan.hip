@@ -223,131 +223,99 @@ struct ScanArgs {
 };
 
 struct __align__(16) ScanSmem {
+  float y[kWaves][kChW * 8][kYStride];   // partial readouts per lane and token (first: short
+                                         // immediate offsets)
   float4 bc[kTT][8];                     // (B_2g, B_2g+1, C_2g, C_2g+1) per token and lane group
   float2 dd[kWaves][kTS][kChW];          // (Delta, Delta*u) per token and channel
-  float y[kWaves][kChW * 8][kYStride];   // partial readouts per lane and token
 };
 
-// One workgroup: 32 channels of one sequence over one chunk of tokens.
+// Per-thread state of one workgroup: 32 channels of one sequence over one chunk of tokens.
 //   lane = 8*c + g: channel c of the wave; g is the state group (states 2g, 2g+1) in the
 //   recurrence, and the token pair (2g, 2g+1 of each 16-token sub-tile) in the element-wise
 //   prologue/epilogue.
 // kMain = true: full forward of the chunk (carry-in, readout, epilogue, last_state).
 // kMain = false: chunk summary (local final state from zero and sum of Delta), no output.
 // kVec: seqlen % 8 == 0 and 16-byte aligned tensors -> vector loads and stores.
-template <typename Tin, bool kMain, bool kVec>
-__global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
+// kSoftplus / kGate: softplus on Delta / z gate present (compile-time, no per-element selects).
+template <typename Tin, bool kMain, bool kVec, bool kSoftplus, bool kGate>
+struct ScanThread {
   using Raw = typename RawPair<Tin>::T;
-  __shared__ ScanSmem sm;
-  const Tin* __restrict__ U = static_cast<const Tin*>(p.u);
-  const Tin* __restrict__ DL = static_cast<const Tin*>(p.delta);
-  const Tin* __restrict__ Bm = static_cast<const Tin*>(p.B);
-  const Tin* __restrict__ Cm = static_cast<const Tin*>(p.C);
-  const Tin* __restrict__ Z = static_cast<const Tin*>(p.z);
-  const bool has_z = kMain && Z != nullptr;
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int c = lane >> 3;
-  const int g = lane & 7;
-
-  const int64_t nwg_ch = (int64_t)p.batch * p.dblocks;
-  const int64_t k = blockIdx.x / nwg_ch;          // chunk
-  const int64_t cb = blockIdx.x - k * nwg_ch;     // channel block
-  const int64_t b = cb / p.dblocks;
-  const int64_t d = (cb - b * p.dblocks) * kChWG + w * kChW + c;
-  const bool dvalid = d < p.dim;
-  const int64_t dd_ = dvalid ? d : 0;
-  const int64_t ch = b * p.dim + dd_;             // flat channel (clamped when invalid)
-  const int64_t row = ch * p.L;
-  const int64_t t_begin = k * p.chunk_len;
-  const int64_t t_end = min(p.L, t_begin + p.chunk_len);
-
-  const float a0 = p.A[dd_ * kN + 2 * g] * kLog2e;
-  const float a1 = p.A[dd_ * kN + 2 * g + 1] * kLog2e;
-  const float bias = p.bias ? p.bias[dd_] : 0.f;
-  const float dskip = (kMain && p.D) ? p.D[dd_] : 0.f;
-
-  float h0 = 0.f, h1 = 0.f;
-  if (kMain && k > 0) {
-    // carry-in: compose the summaries of chunks 0..k-1 in order
-    const int64_t nsum = p.nchunks - 1;
-    const float* S = p.ws_S + ch * nsum;
-    const float* H = p.ws_H + ch * nsum * kN;
-    for (int64_t j = 0; j < k; ++j) {
-      const float s = S[j];
-      h0 = fmaf(fast_exp2(a0 * s), h0, H[j * kN + 2 * g]);
-      h1 = fmaf(fast_exp2(a1 * s), h1, H[j * kN + 2 * g + 1]);
-    }
-  }
-
-  // B/C staging assignment: thread -> (row r of the 32 B/C rows, 8-token segment q)
-  const int sr = tid >> 3;
-  const int sq = tid & 7;
-  const int sn = sr & 15;
-  const Tin* __restrict__ BCrow = (sr < 16 ? Bm : Cm) + (b * kN + sn) * p.L;
-  const int sslot = (sr < 16 ? 0 : 2) + (sn & 1);
-  const int sg = sn >> 1;
-
-  // ---- raw registers, prefetched one tile ahead: sub-tile s of the next tile is loaded as soon
-  // as sub-tile s of the current tile has consumed its registers (no copies), B/C right after
-  // they are staged in LDS.
+  ScanSmem& sm;
+  const Tin* __restrict__ U;
+  const Tin* __restrict__ DL;
+  const Tin* __restrict__ Z;
+  Tin* __restrict__ O;
+  const Tin* __restrict__ BCrow;
+  int w, lane, c, g, sq, sslot, sg;
+  bool dvalid;
+  int64_t row, t_end;
+  float a0, a1, bias, dskip;
+  float h0 = 0.f, h1 = 0.f, dsum = 0.f;
   Raw ru[kSub], rd[kSub], rz[kSub];
   Raw8<Tin> rbc;
-  // Tokens past t_end are never loaded; the remainder test is uniform, so full sub-tiles (all
-  // but the last of a chunk) take the unguarded path.  Lanes of channels >= dim read a valid
-  // row (channel clamped to the block's first) and never store.
-  auto load_sub = [&](int64_t t0, int s) {
-    const int64_t tb = t0 + kTS * s;
-    const int64_t rem = t_end - tb;          // uniform
-    const int64_t t = tb + 2 * g;
-    if (rem >= kTS) {
-      ru[s] = load_pair<kVec>(U, row + t, true, true);
-      rd[s] = load_pair<kVec>(DL, row + t, true, true);
-      if (has_z) rz[s] = load_pair<kVec>(Z, row + t, true, true);
-    } else {
-      const bool ok0 = 2 * g < rem, ok1 = 2 * g + 1 < rem;
-      ru[s] = load_pair<kVec>(U, row + t, ok0, ok1);
-      rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
-      if (has_z) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < kSub; ++s) load_sub(t_begin, s);
-  rbc = load8<kVec>(BCrow, t_begin + 8 * sq, t_begin + 8 * sq, t_end);
 
-  float dsum = 0.f;  // summary kernel: sum of Delta over this lane's tokens
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
-    const int64_t tn = t0 + kTT;      // next tile
-    const bool more = tn < t_end;
+  __device__ __forceinline__ ScanThread(ScanSmem& s) : sm(s) {}
+
+  // raw loads of this lane's token pair in sub-tile s starting at token tb; tokens past t_end
+  // are not loaded (kFull: the whole sub-tile is inside the chunk)
+  template <bool kFull>
+  __device__ __forceinline__ void load_sub(int64_t tb, int s) {
+    const int64_t t = tb + 2 * g;
+    bool ok0 = true, ok1 = true;
+    if (!kFull) {
+      const int64_t rem = t_end - tb;
+      ok0 = 2 * g < rem;
+      ok1 = 2 * g + 1 < rem;
+    }
+    ru[s] = load_pair<kVec>(U, row + t, ok0, ok1);
+    rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
+    if (kGate) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
+  }
+  __device__ __forceinline__ void load_bc(int64_t t0) {
+    rbc = load8<kVec>(BCrow, t0 + 8 * sq, t0 + 8 * sq, t_end);
+  }
+  // prefetch of sub-tile s of the tile starting at tn (uniform branch)
+  __device__ __forceinline__ void prefetch_sub(int64_t tn, int s) {
+    if (tn + kTT <= t_end) load_sub<true>(tn + kTS * s, s);
+    else if (tn < t_end) load_sub<false>(tn + kTS * s, s);
+  }
+
+  // One 64-token tile starting at t0 (kFull: all of it inside the chunk); prefetches the tile
+  // starting at t0 + kTT when that starts before t_end.
+  template <bool kFull>
+  __device__ __forceinline__ void tile(int64_t t0) {
+    const int64_t tn = t0 + kTT;
     __syncthreads();  // every wave is done reading the previous tile's B/C
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       reinterpret_cast<float*>(&sm.bc[8 * sq + i][sg])[sslot] = elem8(rbc, i);
-    if (more) rbc = load8<kVec>(BCrow, tn + 8 * sq, tn + 8 * sq, t_end);
+    if (tn < t_end) load_bc(tn);
     __syncthreads();
 
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
       const int64_t tb = t0 + kTS * s;
-      const int64_t rem = t_end - tb;          // uniform
       const int64_t tp = tb + 2 * g;           // this lane's token pair (prologue/epilogue)
-      const bool ok0 = 2 * g < rem, ok1 = 2 * g + 1 < rem;
+      bool ok0 = true, ok1 = true;
+      if (!kFull) {
+        const int64_t rem = t_end - tb;
+        ok0 = 2 * g < rem;
+        ok1 = 2 * g + 1 < rem;
+      }
       // ---- prologue: Delta = softplus(raw + bias), Delta*u for the lane's two tokens
       const float2 x = unpack(ru[s]);
       const float2 dr = unpack(rd[s]);
-      float2 zz = make_float2(0.f, 0.f);
-      if (has_z) zz = unpack(rz[s]);
-      if (more) load_sub(tn, s);
+      float2 zz;
+      if (kGate) zz = unpack(rz[s]);
+      prefetch_sub(tn, s);
       float dl0 = dr.x + bias, dl1 = dr.y + bias;
-      if (p.softplus) {
+      if (kSoftplus) {
         dl0 = softplus_f32(dl0);
         dl1 = softplus_f32(dl1);
       }
-      if (rem < kTS) {  // tokens past the end of the chunk leave the state unchanged
-        if (!ok0) dl0 = 0.f;
-        if (!ok1) dl1 = 0.f;
+      if (!kFull) {  // tokens past the end of the chunk leave the state unchanged
+        dl0 = ok0 ? dl0 : 0.f;
+        dl1 = ok1 ? dl1 : 0.f;
       }
       if (!kMain) dsum += dl0 + dl1;
       sm.dd[w][2 * g][c] = make_float2(dl0, dl0 * x.x);
@@ -378,43 +346,118 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
 #pragma unroll
         for (int i = 0; i < kTS / 2; ++i) ydst[i] = make_float2(yp[2 * i], yp[2 * i + 1]);
         wave_lds_fence();
-        // ---- epilogue: sum the 8 partial readouts of tokens (2g, 2g+1), skip, gate, store
-        float2 y = make_float2(0.f, 0.f);
+        // ---- epilogue: sum the 8 partial readouts of tokens (2g, 2g+1) as a tree, skip, gate
+        float2 v[8];
 #pragma unroll
-        for (int gg = 0; gg < 8; ++gg) {
-          const float2 v = *reinterpret_cast<const float2*>(&sm.y[w][c * 8 + gg][2 * g]);
-          y.x += v.x;
-          y.y += v.y;
-        }
+        for (int gg = 0; gg < 8; ++gg)
+          v[gg] = *reinterpret_cast<const float2*>(&sm.y[w][c * 8 + gg][2 * g]);
+        float2 y;
+        y.x = ((v[0].x + v[1].x) + (v[2].x + v[3].x)) + ((v[4].x + v[5].x) + (v[6].x + v[7].x));
+        y.y = ((v[0].y + v[1].y) + (v[2].y + v[3].y)) + ((v[4].y + v[5].y) + (v[6].y + v[7].y));
         y.x = fmaf(dskip, x.x, y.x);
         y.y = fmaf(dskip, x.y, y.y);
-        if (has_z) {
+        if (kGate) {
           y.x *= silu_f32(zz.x);
           y.y *= silu_f32(zz.y);
         }
-        store_pair<kVec>(static_cast<Tin*>(p.out), row + tp, y, dvalid && ok0, dvalid && ok1);
+        store_pair<kVec>(O, row + tp, y, dvalid && ok0, dvalid && ok1);
       }
       wave_lds_fence();
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+};
+
+template <typename Tin, bool kMain, bool kVec, bool kSoftplus, bool kGate>
+__global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
+  __shared__ ScanSmem sm;
+  ScanThread<Tin, kMain, kVec, kSoftplus, kGate> th(sm);
+  th.U = static_cast<const Tin*>(p.u);
+  th.DL = static_cast<const Tin*>(p.delta);
+  th.Z = static_cast<const Tin*>(p.z);
+  th.O = static_cast<Tin*>(p.out);
+  const Tin* __restrict__ Bm = static_cast<const Tin*>(p.B);
+  const Tin* __restrict__ Cm = static_cast<const Tin*>(p.C);
+
+  const int tid = threadIdx.x;
+  th.w = tid >> 6;
+  th.lane = tid & 63;
+  th.c = th.lane >> 3;
+  th.g = th.lane & 7;
+  const int g = th.g;
+
+  const int64_t nwg_ch = (int64_t)p.batch * p.dblocks;
+  const int64_t k = blockIdx.x / nwg_ch;          // chunk
+  const int64_t cb = blockIdx.x - k * nwg_ch;     // channel block
+  const int64_t b = cb / p.dblocks;
+  const int64_t d = (cb - b * p.dblocks) * kChWG + th.w * kChW + th.c;
+  // lanes of channels >= dim read a valid row (the block's first channel) and never store
+  th.dvalid = d < p.dim;
+  const int64_t dd_ = th.dvalid ? d : (cb - b * p.dblocks) * kChWG;
+  const int64_t ch = b * p.dim + dd_;
+  th.row = ch * p.L;
+  const int64_t t_begin = k * p.chunk_len;
+  th.t_end = min(p.L, t_begin + p.chunk_len);
+
+  th.a0 = p.A[dd_ * kN + 2 * g] * kLog2e;
+  th.a1 = p.A[dd_ * kN + 2 * g + 1] * kLog2e;
+  th.bias = p.bias ? p.bias[dd_] : 0.f;
+  th.dskip = (kMain && p.D) ? p.D[dd_] : 0.f;
+
+  if (kMain && k > 0) {
+    // carry-in: compose the summaries of chunks 0..k-1 in order
+    const int64_t nsum = p.nchunks - 1;
+    const float* S = p.ws_S + ch * nsum;
+    const float* H = p.ws_H + ch * nsum * kN;
+    float h0 = 0.f, h1 = 0.f;
+    for (int64_t j = 0; j < k; ++j) {
+      const float sd = S[j];
+      h0 = fmaf(fast_exp2(th.a0 * sd), h0, H[j * kN + 2 * g]);
+      h1 = fmaf(fast_exp2(th.a1 * sd), h1, H[j * kN + 2 * g + 1]);
+    }
+    th.h0 = h0;
+    th.h1 = h1;
+  }
+
+  // B/C staging assignment: thread -> (row r of the 32 B/C rows, 8-token segment q)
+  const int sr = tid >> 3;
+  th.sq = tid & 7;
+  const int sn = sr & 15;
+  th.BCrow = (sr < 16 ? Bm : Cm) + (b * kN + sn) * p.L;
+  th.sslot = (sr < 16 ? 0 : 2) + (sn & 1);
+  th.sg = sn >> 1;
+
+  // raw registers are prefetched one tile ahead: sub-tile s of the next tile is loaded as soon
+  // as sub-tile s of the current tile has consumed its registers, B/C right after staging
+  const int64_t t_end = th.t_end;
+  if (t_begin + kTT <= t_end) {
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) th.template load_sub<true>(t_begin + kTS * s, s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) th.template load_sub<false>(t_begin + kTS * s, s);
+  }
+  th.load_bc(t_begin);
+  int64_t t0 = t_begin;
+  for (; t0 + kTT <= t_end; t0 += kTT) th.template tile<true>(t0);
+  if (t0 < t_end) th.template tile<false>(t0);
 
   if (kMain) {
-    if (p.last_state && dvalid && k == p.nchunks - 1) {
-      p.last_state[ch * kN + 2 * g] = h0;
-      p.last_state[ch * kN + 2 * g + 1] = h1;
+    if (p.last_state && th.dvalid && k == p.nchunks - 1) {
+      p.last_state[ch * kN + 2 * g] = th.h0;
+      p.last_state[ch * kN + 2 * g + 1] = th.h1;
     }
   } else {
     // sum of Delta over the chunk: reduce the 8 token-pair lanes of this channel, fixed order
-    float s = dsum;
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (dvalid) {
+    float sd = th.dsum;
+    sd += __shfl_xor(sd, 1);
+    sd += __shfl_xor(sd, 2);
+    sd += __shfl_xor(sd, 4);
+    if (th.dvalid) {
       const int64_t nsum = p.nchunks - 1;
-      p.ws_H[(ch * nsum + k) * kN + 2 * g] = h0;
-      p.ws_H[(ch * nsum + k) * kN + 2 * g + 1] = h1;
-      if (g == 0) p.ws_S[ch * nsum + k] = s;
+      p.ws_H[(ch * nsum + k) * kN + 2 * g] = th.h0;
+      p.ws_H[(ch * nsum + k) * kN + 2 * g + 1] = th.h1;
+      if (g == 0) p.ws_S[ch * nsum + k] = sd;
     }
   }
 }
@@ -531,6 +574,32 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+template <typename Tin, bool kMain, bool kVec, bool kSoftplus, bool kGate>
+int launch_one(dim3 grid, hipStream_t s, const ScanArgs& a) {
+  hipLaunchKernelGGL((scan_kernel<Tin, kMain, kVec, kSoftplus, kGate>), grid, dim3(kThreads), 0,
+                     s, a);
+  return launch_status();
+}
+
+template <typename Tin, bool kMain, bool kVec>
+int launch_flags(bool softplus, bool gate, dim3 grid, hipStream_t s, const ScanArgs& a) {
+  if (!kMain) gate = false;  // the summary pass has no readout
+  if (softplus)
+    return gate ? launch_one<Tin, kMain, kVec, true, kMain>(grid, s, a)
+                : launch_one<Tin, kMain, kVec, true, false>(grid, s, a);
+  return gate ? launch_one<Tin, kMain, kVec, false, kMain>(grid, s, a)
+              : launch_one<Tin, kMain, kVec, false, false>(grid, s, a);
+}
+
+template <bool kMain>
+int launch_scan(bool bf, bool vec, bool softplus, bool gate, dim3 grid, hipStream_t s,
+                const ScanArgs& a) {
+  if (bf) return vec ? launch_flags<uint16_t, kMain, true>(softplus, gate, grid, s, a)
+                     : launch_flags<uint16_t, kMain, false>(softplus, gate, grid, s, a);
+  return vec ? launch_flags<float, kMain, true>(softplus, gate, grid, s, a)
+             : launch_flags<float, kMain, false>(softplus, gate, grid, s, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -576,18 +645,11 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
   if (pl.nchunks > 1) {
     dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
-    if (bf && vec) hipLaunchKernelGGL((scan_kernel<uint16_t, false, true>), grid, dim3(kThreads), 0, s, a);
-    else if (bf) hipLaunchKernelGGL((scan_kernel<uint16_t, false, false>), grid, dim3(kThreads), 0, s, a);
-    else if (vec) hipLaunchKernelGGL((scan_kernel<float, false, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((scan_kernel<float, false, false>), grid, dim3(kThreads), 0, s, a);
-    if (launch_status() != MAMBA_OK) return MAMBA_ERR_HIP;
+    if (launch_scan<false>(bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
+      return MAMBA_ERR_HIP;
   }
   dim3 grid((unsigned)(nwg_ch * pl.nchunks));
-  if (bf && vec) hipLaunchKernelGGL((scan_kernel<uint16_t, true, true>), grid, dim3(kThreads), 0, s, a);
-  else if (bf) hipLaunchKernelGGL((scan_kernel<uint16_t, true, false>), grid, dim3(kThreads), 0, s, a);
-  else if (vec) hipLaunchKernelGGL((scan_kernel<float, true, true>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((scan_kernel<float, true, false>), grid, dim3(kThreads), 0, s, a);
-  return launch_status();
+  return launch_scan<true>(bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const float* A,
