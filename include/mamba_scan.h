@@ -108,7 +108,9 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
  *   B, C             : (batch, dstate), io_dtype
  *   A, D, delta_bias : as for mamba_scan_fwd
  *
- * dims->seqlen must be 1; dims->chunk_len is ignored.  NULL allowed for D, z, delta_bias.
+ * dims->seqlen must be 1 and dims->batch at most 65535 (MAMBA_ERR_SHAPE otherwise);
+ * dims->chunk_len is ignored.  state and A must be 16-byte aligned.  NULL allowed for D, z,
+ * delta_bias.
  */
 int mamba_state_update(float* state, const void* u, const void* delta, const float* A,
                        const void* B, const void* C, const float* D, const void* z,

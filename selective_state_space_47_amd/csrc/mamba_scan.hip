@@ -480,15 +480,15 @@ struct StepArgs {
 };
 
 // Four lanes per channel, four states per lane (one float4 of the state row each); 16 channels
-// per wave, 64 per workgroup.  The step is bound by the state read and write.
+// per wave, 64 per workgroup.  Grid: (channel blocks of 64, batch) -- no integer division.
+// The step is bound by the state read and write.
 template <typename Tin>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int q = threadIdx.x & 3;
-  const int64_t ch = gid >> 2;
-  if (ch >= p.batch * p.dim) return;
-  const int64_t b = ch / p.dim;
-  const int64_t d = ch - b * p.dim;
+  const int64_t d = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  if (d >= p.dim) return;
+  const int64_t b = blockIdx.y;
+  const int64_t ch = b * p.dim + d;
   const Tin* U = static_cast<const Tin*>(p.u);
   const Tin* DL = static_cast<const Tin*>(p.delta);
   const Tin* Bm = static_cast<const Tin*>(p.B);
@@ -668,14 +668,14 @@ int mamba_state_update(float* state, const void* u, const void* delta, const flo
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
   a.bias = delta_bias; a.out = out; a.batch = dims->batch; a.dim = dims->dim;
   a.softplus = softplus_flag ? 1 : 0;
-  const int64_t threads = dims->batch * dims->dim * 4;
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7fffffffLL) return MAMBA_ERR_SHAPE;
+  const int64_t xblocks = (dims->dim + 63) / 64;
+  if (xblocks > 0x7fffffffLL || dims->batch > 65535) return MAMBA_ERR_SHAPE;
+  const dim3 grid((unsigned)xblocks, (unsigned)dims->batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dims->io_dtype == MAMBA_BF16)
-    hipLaunchKernelGGL((step_kernel<uint16_t>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((step_kernel<uint16_t>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((step_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((step_kernel<float>), grid, dim3(256), 0, s, a);
   return launch_status();
 }
 
