@@ -153,6 +153,82 @@ def bench_state_update(steps, torch, binding, synth, dev):
                      "Infinity Cache: effective bandwidth, wall time over back-to-back launches")
 
 
+def device_inputs(w, dev, torch, L=None, seed=0):
+    """Seeded on-device inputs of a workload's shape and distributions (timing only: the parity
+    tests use the host generator in selective_state_space_47_amd.synth)."""
+    from selective_state_space_47_amd import synth
+    L = w.seqlen if L is None else L
+    io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 1000 + seed)
+    shp = (w.batch, w.dim, L)
+    t = {k: torch.randn(shp, generator=g, device=dev, dtype=torch.float32).to(io)
+         for k in ("u", "delta", "z")}
+    for k in ("B", "C"):
+        t[k] = torch.randn((w.batch, w.dstate, L), generator=g, device=dev,
+                           dtype=torch.float32).to(io)
+    A, D, bias = synth.params(w)
+    t["A"], t["D"], t["delta_bias"] = (torch.from_numpy(v).to(dev) for v in (A, D, bias))
+    return t
+
+
+def time_forward(t, torch, binding, reps, warm):
+    """HIP-event time of whole mamba_scan_fwd calls (all of its launches) on the current stream."""
+    u = t["u"]
+    out = torch.empty_like(u)
+    last = torch.empty((u.shape[0], u.shape[1], 16), dtype=torch.float32, device=u.device)
+
+    def call():
+        binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                               t["delta_bias"], True, return_last_state=True, out=out,
+                               last_state=last)
+    for _ in range(warm):
+        call()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2]
+
+
+def other_workloads(torch, binding, synth, dev):
+    """Every other whole-sequence workload, and the sequence-length sweep (batch 1, 1536
+    channels, fp32) for the linear-in-L claim."""
+    res = {}
+    for name in ("tiny", "130m_layer", "1m_steps"):
+        w = synth.WORKLOADS[name]
+        t = device_inputs(w, dev, torch)
+        reps, warm = (5, 2) if name == "1m_steps" else (30, 20)
+        ms = time_forward(t, torch, binding, reps, warm)
+        s = 2 if w.io_dtype == "bf16" else 4
+        nbytes = scan_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s, s)
+        ws = binding.mamba_scan_workspace_bytes(w.batch, w.dim, w.seqlen, t["u"].dtype)
+        res[name] = dict(batch=w.batch, dim=w.dim, seqlen=w.seqlen, io_dtype=w.io_dtype,
+                         us=ms * 1e3, channel_steps_per_s=w.channel_steps / (ms * 1e-3),
+                         alg_GBps=nbytes / (ms * 1e-3) / 1e9,
+                         alu_frac=w.channel_steps * ALU_OPS_PER_CHANNEL_STEP / (ms * 1e-3)
+                         / ALU_PEAK_LANE_OPS,
+                         chunked=ws > 0)
+        del t
+        torch.cuda.empty_cache()
+    sweep = []
+    w = synth.WORKLOADS["1m_steps"]
+    for lg in (11, 13, 15, 17, 19, 20):
+        L = 1 << lg
+        t = device_inputs(w, dev, torch, L=L, seed=lg)
+        ms = time_forward(t, torch, binding, 5 if lg >= 19 else 15, 3)
+        sweep.append(dict(L=L, us=ms * 1e3, channel_steps_per_s=w.dim * L / (ms * 1e-3)))
+        del t
+        torch.cuda.empty_cache()
+    return res, sweep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +239,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-step", action="store_true", help="skip the state-update timing")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads and the sequence-length sweep")
     ap.add_argument("--step-steps", type=int, default=1000)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -283,6 +361,8 @@ def main():
         del t, out
         torch.cuda.empty_cache()
         rec["state_update"] = bench_state_update(args.step_steps, torch, binding, synth, dev)
+    if not args.no_others:
+        rec["other_workloads"], rec["seqlen_sweep"] = other_workloads(torch, binding, synth, dev)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_seconds)
     else:

@@ -554,7 +554,9 @@ int make_plan(const mamba_dims* dm, Plan* pl) {
   const int64_t nwg_ch = dm->batch * pl->dblocks;
   int64_t cl = dm->chunk_len;
   if (cl == 0) {
-    int64_t K = (kTargetWG + nwg_ch - 1) / nwg_ch;
+    // as many chunks as keep every workgroup of the main pass resident at once (5 per CU on
+    // 256 CUs): a second round of a few workgroups would nearly double a long pass
+    int64_t K = kTargetWG / nwg_ch;
     const int64_t maxK = (L + kChunkAlign - 1) / kChunkAlign;
     if (K > maxK) K = maxK;
     if (K < 1) K = 1;
