@@ -184,3 +184,10 @@ def random_case(seed, batch, dim, L, dstate=16, bias_lo=1e-3, bias_hi=1e-1, bf16
     """Small seeded case of arbitrary shape (edge-shape and flag-toggle tests)."""
     w = Workload("case", batch, dim, dstate, L, "bf16" if bf16 else "f32", bias_lo, bias_hi, seed)
     return scan_inputs(w)
+
+
+def selective_copy_values(gap: int, n_seq: int = 400, seed: int = 4705):
+    """Values of the selective-copying experiment: n_seq sequences, each a target scalar followed
+    by `gap` distractors, all N(0, 1) fp32; returns an (n_seq, 1 + gap) array (column 0 is the
+    target).  One generator per gap: SeedSequence([seed, 7, gap])."""
+    return _rng(seed, 7, gap).standard_normal((n_seq, 1 + gap), dtype=np.float32)

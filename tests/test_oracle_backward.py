@@ -1,0 +1,69 @@
+"""Pins of the fp64 backward oracle (CPU): its forward equals the C oracle, and every gradient
+equals central finite differences of the C oracle's forward (an independent implementation)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward
+from selective_state_space_47_amd import synth
+
+
+def _case(seed, batch, dim, L, flags):
+    x = {k: v.astype(np.float64) for k, v in synth.random_case(seed, batch, dim, L).items()}
+    rng = np.random.default_rng(seed + 1)
+    x["dout"] = rng.standard_normal((batch, dim, L))
+    x["dlast"] = rng.standard_normal((batch, dim, 16))
+    if not flags["softplus"]:
+        x["delta"] = np.abs(x["delta"]) * 0.1 + 0.01
+    return x
+
+
+FLAGS = [dict(softplus=True, D=True, z=True, bias=True),
+         dict(softplus=False, D=False, z=False, bias=False),
+         dict(softplus=True, D=False, z=True, bias=False)]
+
+
+def _loss(x, flags, **over):
+    v = dict(x, **over)
+    out, last = oracle.scan_ref(v["u"], v["delta"], v["A"], v["B"], v["C"],
+                                v["D"] if flags["D"] else None, v["z"] if flags["z"] else None,
+                                v["delta_bias"] if flags["bias"] else None, flags["softplus"])
+    return float((out * x["dout"]).sum() + (last * x["dlast"]).sum())
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_backward_oracle_forward_matches_c_oracle(flags):
+    import torch
+    x = _case(3, 2, 3, 21, flags)
+    t = {k: torch.as_tensor(v) for k, v in x.items()}
+    out, last = backward.forward_torch(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                       t["D"] if flags["D"] else None,
+                                       t["z"] if flags["z"] else None,
+                                       t["delta_bias"] if flags["bias"] else None,
+                                       flags["softplus"])
+    ro, rl = oracle.scan_ref(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                             x["D"] if flags["D"] else None, x["z"] if flags["z"] else None,
+                             x["delta_bias"] if flags["bias"] else None, flags["softplus"])
+    np.testing.assert_allclose(out.numpy(), ro, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(last.numpy(), rl, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_backward_oracle_matches_finite_differences(flags):
+    x = _case(5, 2, 3, 17, flags)
+    g = backward.scan_bwd_ref(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                              x["D"] if flags["D"] else None, x["z"] if flags["z"] else None,
+                              x["delta_bias"] if flags["bias"] else None, flags["softplus"],
+                              x["dout"], x["dlast"])
+    rng = np.random.default_rng(9)
+    names = ["u", "delta", "A", "B", "C"] + [n for n, f in (("D", "D"), ("z", "z"),
+                                                             ("delta_bias", "bias")) if flags[f]]
+    eps = 1e-6
+    for n in names:
+        for _ in range(2):
+            v = rng.standard_normal(x[n].shape)
+            fp = _loss(x, flags, **{n: x[n] + eps * v})
+            fm = _loss(x, flags, **{n: x[n] - eps * v})
+            fd = (fp - fm) / (2 * eps)
+            an = float((g["d" + n] * v).sum())
+            assert abs(fd - an) <= 2e-6 * max(1.0, abs(fd)), (n, fd, an)
