@@ -56,6 +56,10 @@ def _load():
             lib.ref_state_update_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
                                                  i64, i64, i64, dp]
             lib.ref_state_update_f64.restype = None
+            lib.ref_scan_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp,
+                                             dp, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
+                                             dp]
+            lib.ref_scan_bwd_f64.restype = None
             lib.ref_affine_scan_f64.argtypes = [dp, dp, i64, ctypes.c_double, dp]
             lib.ref_affine_scan_f64.restype = None
             lib.ref_softplus_f64.argtypes = [ctypes.c_double]
@@ -132,6 +136,35 @@ def state_update_ref(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                                  _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
                                  batch, dim, N, _ptr(out))
     return out, st
+
+
+def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                 dout=None, dlast=None):
+    """Gradients of sum(out * dout) + sum(last_state * dlast) by the hand-written adjoint
+    recurrence in float64 (``ref_scan_bwd_f64``).
+
+    Returns a dict of float64 arrays du, ddelta (w.r.t. the raw delta), dA, dB, dC, dD,
+    ddelta_bias and dz (None without a gate).  dD and ddelta_bias are the gradients for a zero skip
+    or bias when D or delta_bias is None.  dlast=None means zero.
+    """
+    u, delta, A, B, C = (_f64(v) for v in (u, delta, A, B, C))
+    D, z, delta_bias, dout, dlast = (_f64(v) for v in (D, z, delta_bias, dout, dlast))
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    assert N <= 64 and dout is not None and dout.shape == u.shape
+    assert dlast is None or dlast.shape == (batch, dim, N)
+    assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
+    res = {k: np.empty(s, dtype=np.float64) for k, s in (
+        ("du", u.shape), ("ddelta", u.shape), ("dA", (dim, N)), ("dB", B.shape),
+        ("dC", C.shape), ("dD", (dim,)), ("ddelta_bias", (dim,)))}
+    res["dz"] = np.empty(u.shape, dtype=np.float64) if z is not None else None
+    _load().ref_scan_bwd_f64(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                             _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dout),
+                             _ptr(dlast), batch, dim, N, L, _ptr(res["du"]),
+                             _ptr(res["ddelta"]), _ptr(res["dA"]), _ptr(res["dB"]),
+                             _ptr(res["dC"]), _ptr(res["dD"]), _ptr(res["dz"]),
+                             _ptr(res["ddelta_bias"]))
+    return res
 
 
 def affine_scan_ref(a, b, h0=0.0):

@@ -133,3 +133,129 @@ void ref_affine_scan_f64(const double* a, const double* b, int64_t n, double h0,
     h[t] = s;
   }
 }
+
+/*
+ * Gradients of the whole-sequence forward (the backward pass that "activation recomputation"
+ * refers to in "State Spaces, Selectively -- Mamba" (papermap), chapter 01/02), written out as the
+ * adjoint of the recurrence above.  For loss = sum(out * dout) + sum(last_state * dlast):
+ *
+ *   with s = sigmoid(z):  dy_t = dout_t * z_t * s       (dy_t = dout_t without a gate)
+ *                         dz_t = dout_t * ypre_t * s * (1 + z_t * (1 - s)),  ypre_t = sum_n C h_t + D u_t
+ *   lam_t[n] = dy_t * C[n,t] + Abar_{t+1}[n] * lam_{t+1}[n],   lam_{L-1} carry = dlast
+ *   h_t = Abar_t h_{t-1} + Delta_t B_t u_t  gives
+ *     dDelta_t  = sum_n lam_t (Abar_t A_n h_{t-1} + B_t u_t);  dDelta_raw = dDelta * softplus'(raw + bias)
+ *     dA[d,n]  += lam_t Abar_t Delta_t h_{t-1}
+ *     dB[b,n,t] += lam_t Delta_t u_t          (summed over channels d)
+ *     dC[b,n,t] += dy_t h_t                   (summed over channels d)
+ *     du_t      = dy_t D + sum_n lam_t Delta_t B_t
+ *     dD[d]    += dy_t u_t;   ddelta_bias[d] += dDelta_raw_t
+ *
+ * Every h_t of a channel is stored by a plain forward loop (no recomputation scheme).  Parallel
+ * over channels d (each thread owns whole rows of dA, dD, ddelta_bias); dB and dC are summed into
+ * one buffer per thread, added in thread order at the end.  dlast may be NULL (zero); dz is written
+ * only when z is given; dD and ddelta_bias are always written (the gradient for a zero skip or
+ * bias when D or delta_bias is NULL).
+ */
+void ref_scan_bwd_f64(const double* u, const double* delta, const double* A, const double* B,
+                      const double* C, const double* D, const double* z, const double* delta_bias,
+                      int softplus_flag, const double* dout, const double* dlast, int64_t batch,
+                      int64_t dim, int64_t N, int64_t L, double* du, double* ddelta, double* dA,
+                      double* dB, double* dC, double* dD, double* dz, double* ddelta_bias) {
+  const int64_t nbc = batch * N * L;
+  int nthreads = 1;
+#ifdef _OPENMP
+  nthreads = omp_get_max_threads();
+#endif
+  double* pB = (double*)calloc((size_t)nthreads * (size_t)nbc, sizeof(double));
+  double* pC = (double*)calloc((size_t)nthreads * (size_t)nbc, sizeof(double));
+#pragma omp parallel num_threads(nthreads)
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* myB = pB + (size_t)tid * (size_t)nbc;
+    double* myC = pC + (size_t)tid * (size_t)nbc;
+    double* H = (double*)malloc((size_t)L * (size_t)N * sizeof(double));
+    double* dtv = (double*)malloc((size_t)L * sizeof(double));
+    double* sig = (double*)malloc((size_t)L * sizeof(double));
+    double* ypre = (double*)malloc((size_t)L * sizeof(double));
+    double* lam = (double*)malloc((size_t)N * sizeof(double));
+#pragma omp for schedule(static)
+    for (int64_t d = 0; d < dim; ++d) {
+      const double* Arow = A + d * N;
+      const double bias = delta_bias ? delta_bias[d] : 0.0;
+      const double Dd = D ? D[d] : 0.0;
+      double gA[64];
+      for (int64_t n = 0; n < N; ++n) gA[n] = 0.0;
+      double gD = 0.0, gbias = 0.0;
+      for (int64_t b = 0; b < batch; ++b) {
+        const int64_t row = (b * dim + d) * L;
+        const double* Bb = B + b * N * L;
+        const double* Cb = C + b * N * L;
+        /* forward, keeping every state */
+        for (int64_t t = 0; t < L; ++t) {
+          const double raw = delta[row + t] + bias;
+          dtv[t] = softplus_flag ? sp(raw) : raw;
+          sig[t] = softplus_flag ? 1.0 / (1.0 + exp(-raw)) : 1.0;
+          double y = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double hp = t > 0 ? H[(t - 1) * N + n] : 0.0;
+            const double h = exp(dtv[t] * Arow[n]) * hp + dtv[t] * Bb[n * L + t] * u[row + t];
+            H[t * N + n] = h;
+            y += Cb[n * L + t] * h;
+          }
+          ypre[t] = y + Dd * u[row + t];
+        }
+        /* reverse: adjoint recurrence */
+        for (int64_t n = 0; n < N; ++n) lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          const double x = u[row + t], dt = dtv[t];
+          double dy = dout[row + t];
+          if (z) {
+            const double zz = z[row + t];
+            const double s = 1.0 / (1.0 + exp(-zz));
+            dz[row + t] = dout[row + t] * ypre[t] * s * (1.0 + zz * (1.0 - s));
+            dy = dout[row + t] * zz * s;
+          }
+          gD += dy * x;
+          double gu = dy * Dd, gdt = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            const double l = dy * Cb[n * L + t] + lam[n];
+            const double hp = t > 0 ? H[(t - 1) * N + n] : 0.0;
+            const double a_t = exp(dt * Arow[n]);
+            gdt += l * (a_t * Arow[n] * hp + Bb[n * L + t] * x);
+            gA[n] += l * a_t * dt * hp;
+            myB[(b * N + n) * L + t] += l * dt * x;
+            gu += l * dt * Bb[n * L + t];
+            myC[(b * N + n) * L + t] += dy * H[t * N + n];
+            lam[n] = l * a_t;
+          }
+          const double graw = gdt * sig[t];
+          du[row + t] = gu;
+          ddelta[row + t] = graw;
+          gbias += graw;
+        }
+      }
+      for (int64_t n = 0; n < N; ++n) dA[d * N + n] = gA[n];
+      dD[d] = gD;
+      ddelta_bias[d] = gbias;
+    }
+    free(H);
+    free(dtv);
+    free(sig);
+    free(ypre);
+    free(lam);
+  }
+  for (int64_t i = 0; i < nbc; ++i) {
+    double sb = 0.0, sc = 0.0;
+    for (int t = 0; t < nthreads; ++t) {
+      sb += pB[(size_t)t * (size_t)nbc + i];
+      sc += pC[(size_t)t * (size_t)nbc + i];
+    }
+    dB[i] = sb;
+    dC[i] = sc;
+  }
+  free(pB);
+  free(pC);
+}

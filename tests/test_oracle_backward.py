@@ -67,3 +67,28 @@ def test_backward_oracle_matches_finite_differences(flags):
             fd = (fp - fm) / (2 * eps)
             an = float((g["d" + n] * v).sum())
             assert abs(fd - an) <= 2e-6 * max(1.0, abs(fd)), (n, fd, an)
+
+
+@pytest.mark.parametrize("flags", FLAGS + [dict(softplus=True, D=True, z=False, bias=True)])
+@pytest.mark.parametrize("shape", [(2, 3, 17), (3, 2, 40), (1, 1, 1)])
+def test_c_adjoint_matches_autograd(flags, shape):
+    """The hand-written adjoint recurrence (C) equals autograd of the plain torch forward: two
+    independent derivations of the same gradients.  Absent D / bias: the C oracle still reports
+    the gradient for a zero skip / bias, which autograd gives at D = 0 / bias = 0."""
+    batch, dim, L = shape
+    x = _case(11 + L, batch, dim, L, flags)
+    D = x["D"] if flags["D"] else np.zeros(dim)
+    bias = x["delta_bias"] if flags["bias"] else np.zeros(dim)
+    for dlast in (x["dlast"], None):
+        c = oracle.scan_bwd_ref(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                x["D"] if flags["D"] else None, x["z"] if flags["z"] else None,
+                                x["delta_bias"] if flags["bias"] else None, flags["softplus"],
+                                x["dout"], dlast)
+        t = backward.scan_bwd_ref(x["u"], x["delta"], x["A"], x["B"], x["C"], D,
+                                  x["z"] if flags["z"] else None, bias, flags["softplus"],
+                                  x["dout"], dlast)
+        for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias", "dz"):
+            if k == "dz" and not flags["z"]:
+                assert c[k] is None
+                continue
+            np.testing.assert_allclose(c[k], t[k], rtol=1e-11, atol=1e-12, err_msg=k)

@@ -91,3 +91,42 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
         except AssertionError:
             failures += 1
     assert failures > 0, f"no pin catches the planted mistake {name}"
+
+
+# planted mistakes in the hand-written adjoint (ref_scan_bwd_f64)
+BWD_MUTANTS = [
+    ("bwd_carry_without_abar", "lam[n] = l * a_t;", "lam[n] = l;"),
+    ("bwd_dA_without_delta", "gA[n] += l * a_t * dt * hp;", "gA[n] += l * a_t * hp;"),
+    ("bwd_ddelta_drops_input_term", "gdt += l * (a_t * Arow[n] * hp + Bb[n * L + t] * x);",
+     "gdt += l * (a_t * Arow[n] * hp);"),
+    ("bwd_dC_uses_previous_state", "myC[(b * N + n) * L + t] += dy * H[t * N + n];",
+     "myC[(b * N + n) * L + t] += dy * hp;"),
+    ("bwd_dlast_ignored", "lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;",
+     "lam[n] = 0.0;"),
+    ("bwd_no_softplus_derivative", "const double graw = gdt * sig[t];",
+     "const double graw = gdt;"),
+    ("bwd_gate_derivative_is_sigmoid",
+     "dz[row + t] = dout[row + t] * ypre[t] * s * (1.0 + zz * (1.0 - s));",
+     "dz[row + t] = dout[row + t] * ypre[t] * s;"),
+    ("bwd_du_skip_dropped", "double gu = dy * Dd, gdt = 0.0;", "double gu = 0.0, gdt = 0.0;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_planted_adjoint_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    from tests import test_oracle_backward as bw
+    so = _build_mutant(tmp_path, name, old, new)
+    real = oracle._load()
+    mut = ctypes.CDLL(so)
+    for fn in ("ref_scan_bwd_f64", "ref_scan_fwd_f64", "ref_set_threads", "ref_max_threads"):
+        f = getattr(mut, fn)
+        f.argtypes = getattr(real, fn).argtypes
+        f.restype = getattr(real, fn).restype
+    monkeypatch.setattr(oracle, "_lib", mut)
+    failures = 0
+    for flags in bw.FLAGS + [dict(softplus=True, D=True, z=False, bias=True)]:
+        try:
+            bw.test_c_adjoint_matches_autograd(flags, (2, 3, 17))
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no pin catches the planted mistake {name}"
