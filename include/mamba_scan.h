@@ -1,10 +1,11 @@
 /*
  * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Two operations, both from the discrete selective state-space model:
+ * Three operations, all from the discrete selective state-space model:
  *
  *   mamba_scan_fwd      the whole-sequence forward ("scan") over known tokens;
- *   mamba_state_update  one generation step for one new token per sequence.
+ *   mamba_state_update  one generation step for one new token per sequence;
+ *   mamba_scan_bwd      the gradients of mamba_scan_fwd (training), recomputing the state.
  *
  * The model (sources by page title and section):
  *   - "Mamba" (elemedex dex entry), "How it works": h_t = Abar*h_{t-1} + Bbar*x_t, y_t = C*h_t,
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 1
+#define MAMBA_SCAN_ABI_VERSION 2
 
 enum mamba_status {
   MAMBA_OK = 0,
@@ -56,7 +57,7 @@ enum mamba_status {
   MAMBA_ERR_DTYPE = -3,       /* io_dtype is not one of enum mamba_dtype */
   MAMBA_ERR_UNSUPPORTED = -4, /* dstate != 16 */
   MAMBA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size */
-  MAMBA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than mamba_scan_workspace_bytes() */
+  MAMBA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes() query */
   MAMBA_ERR_HIP = -7          /* the HIP runtime rejected a launch */
 };
 
@@ -116,6 +117,49 @@ int mamba_state_update(float* state, const void* u, const void* delta, const flo
                        const void* B, const void* C, const float* D, const void* z,
                        const float* delta_bias, int softplus_flag, void* out,
                        const mamba_dims* dims, void* stream);
+
+/* Bytes of device workspace mamba_scan_bwd needs for these dims (0 for invalid dims).  It holds
+ * the recomputation checkpoints (64 bytes per channel and 8 tokens), the per-workgroup channel sums
+ * of dB and dC (128 bytes per 32 channels and token) and small per-chunk records. */
+size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims);
+
+/*
+ * Gradients of mamba_scan_fwd (same inputs and flags) for the loss
+ *     sum(out * dout) + sum(last_state * dlast),
+ * sources: "State Spaces, Selectively -- Mamba" (papermap), chapters 01/02 (the scan is trained
+ * with activation recomputation: the backward recomputes the expanded state instead of storing
+ * it); "Mamba remembers by forgetting, read closely" (interactiveml.org), composition equation
+ * (the adjoint of the affine recurrence is an affine recurrence run backwards in time, so chunks
+ * compose their carries the same way).  Per element, with lam the adjoint of h:
+ *     lam_t = dy_t C_t + Abar_{t+1} lam_{t+1} (lam after the last token = dlast),
+ *     dy_t = dout_t silu(z_t),  dz_t = dout_t (sum_n C h_t + D u_t) silu'(z_t),
+ *     ddelta_t = sigmoid(raw_t + bias) * sum_n lam_t (Abar_t A_n h_{t-1} + B_t u_t)
+ *                (without softplus the sigmoid factor is 1),
+ *     du_t = dy_t D + Delta_t sum_n lam_t B_t,  dA = sum_{b,t} lam_t Abar_t Delta_t h_{t-1},
+ *     dB[b,n,t] = sum_d lam_t Delta_t u_t,  dC[b,n,t] = sum_d dy_t h_t,
+ *     dD = sum_{b,t} dy_t u_t,  ddelta_bias = sum_{b,t} ddelta_t.
+ *
+ *   inputs           : as for mamba_scan_fwd (u, delta, A, B, C, D, z, delta_bias, softplus_flag)
+ *   dout             : (batch, dim, seqlen), io_dtype -- gradient of out
+ *   dlast            : (batch, dim, dstate) fp32 -- gradient of last_state; NULL = zero
+ *   du, ddelta, dz   : (batch, dim, seqlen), io_dtype; ddelta is w.r.t. the raw delta input
+ *   dB, dC           : (batch, dstate, seqlen), io_dtype
+ *   dA               : (dim, dstate) fp32
+ *   dD, ddelta_bias  : (dim) fp32; may be NULL (not written).  Written also when D / delta_bias is
+ *                      NULL: then they are the gradients for a zero skip / zero bias.
+ *   workspace        : >= mamba_scan_bwd_workspace_bytes(dims) bytes, 16-byte aligned; contents on
+ *                      entry are ignored
+ *
+ * dz must be non-NULL when z is given and is ignored otherwise.  Every output is overwritten (not
+ * accumulated).  Sums over channels, tokens and sequences are taken in a fixed order, so results
+ * are bitwise reproducible for fixed dims (including chunk_len).  Arithmetic is fp32.
+ */
+int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                   const void* dout, const float* dlast, void* du, void* ddelta, float* dA,
+                   void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                   const mamba_dims* dims, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* mamba_status_string(int status);

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmamba_scan.so")
-SOURCES = [os.path.join(CSRC, "mamba_scan.hip")]
+SOURCES = [os.path.join(CSRC, "mamba_scan.hip"), os.path.join(CSRC, "mamba_scan_bwd.hip")]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

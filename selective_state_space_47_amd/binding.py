@@ -30,7 +30,8 @@ class mamba_dims(ctypes.Structure):
 
 
 EXPORTS = ("mamba_scan_fwd", "mamba_state_update", "mamba_scan_workspace_bytes",
-           "mamba_status_string", "mamba_abi_version")
+           "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_status_string",
+           "mamba_abi_version")
 
 
 def library_path() -> str:
@@ -58,6 +59,12 @@ def lib():
             L.mamba_state_update.restype = ctypes.c_int
             L.mamba_scan_workspace_bytes.argtypes = [dp]
             L.mamba_scan_workspace_bytes.restype = ctypes.c_size_t
+            L.mamba_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp, fp,
+                                         vp, vp, fp, vp, vp, fp, vp, fp, dp, vp,
+                                         ctypes.c_size_t, vp]
+            L.mamba_scan_bwd.restype = ctypes.c_int
+            L.mamba_scan_bwd_workspace_bytes.argtypes = [dp]
+            L.mamba_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
             L.mamba_status_string.argtypes = [ctypes.c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             L.mamba_abi_version.argtypes = []
@@ -197,3 +204,70 @@ def mamba_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None
                                   _ptr(out), ctypes.byref(dm), stream)
     _raise(st)
     return out
+
+
+def mamba_scan_bwd_workspace_bytes(batch, dim, seqlen, io_dtype=torch.float32, dstate=DSTATE,
+                                   chunk_len=0) -> int:
+    code = io_dtype if isinstance(io_dtype, int) else _io_code(io_dtype)
+    dm = make_dims(batch, dim, seqlen, code, dstate, chunk_len)
+    return int(lib().mamba_scan_bwd_workspace_bytes(ctypes.byref(dm)))
+
+
+def mamba_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   dout=None, dlast=None, chunk_len=0, workspace=None, grads=None):
+    """Gradients of mamba_scan_fwd (see mamba_scan_bwd in include/mamba_scan.h).
+
+    Same inputs as mamba_scan_fwd plus dout (batch, dim, L) in the io dtype and optionally dlast
+    (batch, dim, 16) float32.  Returns a dict with du, ddelta, dz (io dtype, dz None without z),
+    dB, dC (io dtype), dA, dD, ddelta_bias (float32; dD / ddelta_bias None when D / delta_bias is
+    None).  `grads` may hold preallocated output tensors under the same keys.
+    """
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, L = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io = u.dtype
+    code = _io_code(io)
+    if dout is None:
+        raise ValueError("dout is required")
+    for t, name, shape in ((u, "u", (batch, dim, L)), (delta, "delta", (batch, dim, L)),
+                           (z, "z", (batch, dim, L)), (dout, "dout", (batch, dim, L)),
+                           (B, "B", (batch, DSTATE, L)), (C, "C", (batch, DSTATE, L))):
+        _check(t, name, shape, io, dev)
+    _check(A, "A", (dim, DSTATE), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _check(dlast, "dlast", (batch, dim, DSTATE), torch.float32, dev)
+    g = dict(grads or {})
+    spec = {"du": ((batch, dim, L), io), "ddelta": ((batch, dim, L), io),
+            "dB": ((batch, DSTATE, L), io), "dC": ((batch, DSTATE, L), io),
+            "dA": ((dim, DSTATE), torch.float32)}
+    if z is not None:
+        spec["dz"] = ((batch, dim, L), io)
+    if D is not None:
+        spec["dD"] = ((dim,), torch.float32)
+    if delta_bias is not None:
+        spec["ddelta_bias"] = ((dim,), torch.float32)
+    for k, (shape, dt) in spec.items():
+        if g.get(k) is None:
+            g[k] = torch.empty(shape, dtype=dt, device=dev)
+        _check(g[k], k, shape, dt, dev)
+    for k in ("dz", "dD", "ddelta_bias"):
+        if k not in spec:
+            g[k] = None
+    dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+    L_ = lib()
+    ws_bytes = int(L_.mamba_scan_bwd_workspace_bytes(ctypes.byref(dm)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = L_.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                           _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dout), _ptr(dlast),
+                           _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                           _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
+                           ctypes.byref(dm), _ptr(workspace), ws_len, stream)
+    _raise(st)
+    return {k: g[k] for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias")}

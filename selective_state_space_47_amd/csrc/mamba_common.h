@@ -1,0 +1,263 @@
+// mamba_common.h -- device helpers, launch arguments and host-side validation shared by the
+// forward/step kernels (mamba_scan.hip) and the backward kernels (mamba_scan_bwd.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mamba_scan.h"
+
+namespace mamba {
+
+constexpr int kN = 16;                 // state size (fixed)
+constexpr int kTT = 64;                // tokens per tile (global loads, B/C staging)
+constexpr int kTS = 16;                // tokens per sub-tile (recurrence, readout reduction)
+constexpr int kSub = kTT / kTS;
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kChW = 8;                // channels per wave
+constexpr int kChWG = kWaves * kChW;   // channels per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kYStride = 18;           // floats per lane slot of the partial-readout buffer
+                                       // (18: b64 writes and reads both bank-conflict free)
+constexpr int kChunkAlign = 16;        // chunk lengths are multiples of this
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTargetWG = 1280;        // 5 workgroups of 4 waves per CU on 256 CUs
+
+// ------------------------------------------------------------------ element access
+//
+// Tokens are handled in pairs (t, t+1) with t even.  Raw pairs stay in registers between the
+// prefetch and their use: a uint32 holding two bf16, or a float2.
+
+template <typename Tin> struct RawPair;
+template <> struct RawPair<uint16_t> { using T = uint32_t; };
+template <> struct RawPair<float> { using T = float2; };
+
+__device__ __forceinline__ float2 unpack(uint32_t w) {
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+__device__ __forceinline__ float2 unpack(float2 v) { return v; }
+__device__ __forceinline__ float unpack1(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float unpack1(float v) { return v; }
+
+template <bool kVec>
+__device__ __forceinline__ uint32_t load_pair(const uint16_t* p, int64_t i, bool ok0, bool ok1) {
+  if (kVec) return ok0 ? *reinterpret_cast<const uint32_t*>(p + i) : 0u;
+  uint32_t lo = ok0 ? p[i] : 0u, hi = ok1 ? p[i + 1] : 0u;
+  return lo | (hi << 16);
+}
+template <bool kVec>
+__device__ __forceinline__ float2 load_pair(const float* p, int64_t i, bool ok0, bool ok1) {
+  if (kVec) return ok0 ? *reinterpret_cast<const float2*>(p + i) : make_float2(0.f, 0.f);
+  return make_float2(ok0 ? p[i] : 0.f, ok1 ? p[i + 1] : 0.f);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> two bf16 in one dword with v_cvt_pk_bf16_f32 (round to nearest, ties to even)
+__device__ __forceinline__ uint32_t pack_bf16(float2 v) {
+  const f32x2_t f = {v.x, v.y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// single-element access (state-update kernel)
+__device__ __forceinline__ float ld_f32(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_f32(const uint16_t* p, int64_t i) { return unpack1(p[i]); }
+__device__ __forceinline__ void st_out(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) {
+  p[i] = (uint16_t)(pack_bf16(make_float2(v, 0.f)) & 0xffffu);
+}
+
+template <bool kVec>
+__device__ __forceinline__ void store_pair(uint16_t* p, int64_t i, float2 v, bool ok0, bool ok1) {
+  const uint32_t w = pack_bf16(v);
+  if (kVec) {
+    if (ok0) *reinterpret_cast<uint32_t*>(p + i) = w;
+  } else {
+    if (ok0) p[i] = (uint16_t)(w & 0xffffu);
+    if (ok1) p[i + 1] = (uint16_t)(w >> 16);
+  }
+}
+template <bool kVec>
+__device__ __forceinline__ void store_pair(float* p, int64_t i, float2 v, bool ok0, bool ok1) {
+  if (kVec) {
+    if (ok0) *reinterpret_cast<float2*>(p + i) = v;
+  } else {
+    if (ok0) p[i] = v.x;
+    if (ok1) p[i + 1] = v.y;
+  }
+}
+
+// Eight consecutive B or C values of one row (tokens t..t+7) for the LDS staging, kept raw in
+// registers until they are written to LDS.
+template <typename Tin> struct Raw8;
+template <> struct Raw8<uint16_t> { uint4 v; };
+template <> struct Raw8<float> { float4 a, b; };
+
+template <bool kVec>
+__device__ __forceinline__ Raw8<uint16_t> load8(const uint16_t* p, int64_t i, int64_t t,
+                                                int64_t t_end) {
+  Raw8<uint16_t> r;
+  if (kVec) {
+    r.v = (t < t_end) ? *reinterpret_cast<const uint4*>(p + i) : make_uint4(0, 0, 0, 0);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = (t + 2 * k < t_end) ? p[i + 2 * k] : 0u;
+      const uint32_t hi = (t + 2 * k + 1 < t_end) ? p[i + 2 * k + 1] : 0u;
+      w[k] = lo | (hi << 16);
+    }
+    r.v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return r;
+}
+template <bool kVec>
+__device__ __forceinline__ Raw8<float> load8(const float* p, int64_t i, int64_t t,
+                                             int64_t t_end) {
+  Raw8<float> r;
+  if (kVec) {
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.a = (t < t_end) ? *reinterpret_cast<const float4*>(p + i) : zero;
+    r.b = (t < t_end) ? *reinterpret_cast<const float4*>(p + i + 4) : zero;
+  } else {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (t + k < t_end) ? p[i + k] : 0.f;
+    r.a = make_float4(v[0], v[1], v[2], v[3]);
+    r.b = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  return r;
+}
+__device__ __forceinline__ float elem8(const Raw8<uint16_t>& r, int k) {
+  const uint32_t ws = (k >> 1) == 0 ? r.v.x : (k >> 1) == 1 ? r.v.y : (k >> 1) == 2 ? r.v.z : r.v.w;
+  return (k & 1) ? __uint_as_float(ws & 0xffff0000u) : __uint_as_float(ws << 16);
+}
+__device__ __forceinline__ float elem8(const Raw8<float>& r, int k) {
+  const float4 q = k < 4 ? r.a : r.b;
+  const int j = k & 3;
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+}
+
+// ------------------------------------------------------------------ scalar math
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// softplus(x) = max(x, 0) + log1p(e), e = exp(-|x|) in (0, 1].  log1p(e) is ln2*log2(u) for
+// u = 1 + e (rounded) plus the rounding error d = e - (u - 1), which is exact (Sterbenz) and
+// |d| <= 2^-24: log(1+e) = log(u) + d/u + O(d^2), and using d for d/u errs by at most
+// |d|(1 - 1/u) < 3e-8 absolute, relative to log1p(e) < 6e-8.  v_log_f32 is relatively accurate
+// near 1 on gfx950 (measured 1.1e-7), so the result is accurate to ~1e-6 relative over the
+// fp32 range (dominated by the rounding of -|x|*log2(e) for large |x|).  max(x, 0) is formed as
+// (x + |x|)/2; NaN propagates; for large x, e underflows and the result is x.
+__device__ __forceinline__ float softplus_f32(float x) {
+  const float e = fast_exp2(-fabsf(x) * kLog2e);
+  const float u = 1.f + e;
+  const float d = e - (u - 1.f);
+  const float l = fmaf(__builtin_amdgcn_logf(u), kLn2, d);
+  return fmaf(0.5f, x + fabsf(x), l);
+}
+
+// silu(z) = z / (1 + exp(-z)).
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-z * kLog2e));
+}
+
+// Keeps the compiler from moving LDS accesses across this point.  Within one wavefront the
+// hardware executes LDS instructions in issue order, so this orders cross-lane exchanges
+// through LDS inside a wave.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ forward launch arguments
+
+struct ScanArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  void* out;
+  float* last_state;
+  float* ws_S;   // (batch*dim, nchunks-1): sum of Delta over the chunk
+  float* ws_H;   // (batch*dim, nchunks-1, 16): chunk-local final state from h = 0
+  float* ckpt;   // (batch*dim, ceil(L/8), 16): state before token 8j (checkpoint mode only)
+  int64_t batch, dim, L;
+  int64_t chunk_len;
+  int64_t nblk8;  // ceil(L / 8)
+  int32_t nchunks;
+  int32_t dblocks;  // ceil(dim / kChWG)
+  int32_t softplus;
+};
+
+// forward kernel modes
+constexpr int kModeSummary = 0;  // chunk summary: local final state from zero and sum of Delta
+constexpr int kModeMain = 1;     // full forward: carry-in, readout, epilogue, last_state
+constexpr int kModeCkpt = 2;     // state before every 8th token, for the backward (no readout)
+
+// ------------------------------------------------------------------ host: validation and plan
+
+struct Plan {
+  int64_t chunk_len;
+  int64_t nchunks;
+  int64_t dblocks;
+  size_t ws_bytes;
+};
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int check_dims(const mamba_dims* dm, bool step) {
+  if (!dm) return MAMBA_ERR_NULL;
+  if (dm->io_dtype != MAMBA_F32 && dm->io_dtype != MAMBA_BF16) return MAMBA_ERR_DTYPE;
+  if (dm->batch <= 0 || dm->dim <= 0 || dm->dstate <= 0 || dm->seqlen <= 0)
+    return MAMBA_ERR_SHAPE;
+  if (dm->dstate != kN) return MAMBA_ERR_UNSUPPORTED;
+  if (step && dm->seqlen != 1) return MAMBA_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 40;  // elements per tensor
+  if (dm->batch > lim || dm->dim > lim || dm->seqlen > lim) return MAMBA_ERR_SHAPE;
+  if ((double)dm->batch * (double)dm->dim * (double)dm->seqlen > (double)lim)
+    return MAMBA_ERR_SHAPE;
+  if (!step && (dm->chunk_len < 0 || dm->chunk_len % kChunkAlign != 0)) return MAMBA_ERR_SHAPE;
+  return MAMBA_OK;
+}
+
+inline int make_plan(const mamba_dims* dm, Plan* pl) {
+  const int64_t L = dm->seqlen;
+  pl->dblocks = (dm->dim + kChWG - 1) / kChWG;
+  const int64_t nwg_ch = dm->batch * pl->dblocks;
+  int64_t cl = dm->chunk_len;
+  if (cl == 0) {
+    // as many chunks as keep every workgroup of the main pass resident at once (5 per CU on
+    // 256 CUs): a second round of a few workgroups would nearly double a long pass
+    int64_t K = kTargetWG / nwg_ch;
+    const int64_t maxK = (L + kChunkAlign - 1) / kChunkAlign;
+    if (K > maxK) K = maxK;
+    if (K < 1) K = 1;
+    cl = ((L + K - 1) / K + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+  }
+  pl->chunk_len = cl;
+  pl->nchunks = (L + cl - 1) / cl;
+  if (pl->nchunks * nwg_ch > 0x7fffffffLL) return MAMBA_ERR_SHAPE;
+  pl->ws_bytes = pl->nchunks > 1
+                     ? (size_t)(dm->batch * dm->dim) * (size_t)(pl->nchunks - 1) * (kN + 1) *
+                           sizeof(float)
+                     : 0;
+  return MAMBA_OK;
+}
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+// Launches the forward kernel in `mode` (defined with the forward kernels).
+__attribute__((visibility("hidden"))) int launch_fwd(int mode, bool bf, bool vec, bool softplus,
+                                                     bool gate, dim3 grid, hipStream_t s,
+                                                     const ScanArgs& a);
+
+}  // namespace mamba

@@ -29,198 +29,11 @@
 //    and chunk, the chunk's local final state (from h = 0) and sum of Delta, i.e. the affine
 //    summary (prod Abar = exp(A * sum Delta), h_local).  The main kernel composes the summaries
 //    of all earlier chunks in order to get its carry-in state, then runs its chunk.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "mamba_common.h"
 
-#include "mamba_scan.h"
-
-namespace {
-
-constexpr int kN = 16;                 // state size (fixed)
-constexpr int kTT = 64;                // tokens per tile (global loads, B/C staging)
-constexpr int kTS = 16;                // tokens per sub-tile (recurrence, readout reduction)
-constexpr int kSub = kTT / kTS;
-constexpr int kWaves = 4;              // waves per workgroup
-constexpr int kChW = 8;                // channels per wave
-constexpr int kChWG = kWaves * kChW;   // channels per workgroup
-constexpr int kThreads = kWaves * 64;
-constexpr int kYStride = 18;           // floats per lane slot of the partial-readout buffer
-                                       // (18: b64 writes and reads both bank-conflict free)
-constexpr int kChunkAlign = 16;        // chunk lengths are multiples of this
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTargetWG = 1280;        // 5 workgroups of 4 waves per CU on 256 CUs
-
-// ------------------------------------------------------------------ element access
-//
-// Tokens are handled in pairs (t, t+1) with t even.  Raw pairs stay in registers between the
-// prefetch and their use: a uint32 holding two bf16, or a float2.
-
-template <typename Tin> struct RawPair;
-template <> struct RawPair<uint16_t> { using T = uint32_t; };
-template <> struct RawPair<float> { using T = float2; };
-
-__device__ __forceinline__ float2 unpack(uint32_t w) {
-  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-}
-__device__ __forceinline__ float2 unpack(float2 v) { return v; }
-__device__ __forceinline__ float unpack1(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-__device__ __forceinline__ float unpack1(float v) { return v; }
-
-template <bool kVec>
-__device__ __forceinline__ uint32_t load_pair(const uint16_t* p, int64_t i, bool ok0, bool ok1) {
-  if (kVec) return ok0 ? *reinterpret_cast<const uint32_t*>(p + i) : 0u;
-  uint32_t lo = ok0 ? p[i] : 0u, hi = ok1 ? p[i + 1] : 0u;
-  return lo | (hi << 16);
-}
-template <bool kVec>
-__device__ __forceinline__ float2 load_pair(const float* p, int64_t i, bool ok0, bool ok1) {
-  if (kVec) return ok0 ? *reinterpret_cast<const float2*>(p + i) : make_float2(0.f, 0.f);
-  return make_float2(ok0 ? p[i] : 0.f, ok1 ? p[i + 1] : 0.f);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// fp32 pair -> two bf16 in one dword with v_cvt_pk_bf16_f32 (round to nearest, ties to even)
-__device__ __forceinline__ uint32_t pack_bf16(float2 v) {
-  const f32x2_t f = {v.x, v.y};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// single-element access (state-update kernel)
-__device__ __forceinline__ float ld_f32(const float* p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float ld_f32(const uint16_t* p, int64_t i) { return unpack1(p[i]); }
-__device__ __forceinline__ void st_out(float* p, int64_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) {
-  p[i] = (uint16_t)(pack_bf16(make_float2(v, 0.f)) & 0xffffu);
-}
-
-template <bool kVec>
-__device__ __forceinline__ void store_pair(uint16_t* p, int64_t i, float2 v, bool ok0, bool ok1) {
-  const uint32_t w = pack_bf16(v);
-  if (kVec) {
-    if (ok0) *reinterpret_cast<uint32_t*>(p + i) = w;
-  } else {
-    if (ok0) p[i] = (uint16_t)(w & 0xffffu);
-    if (ok1) p[i + 1] = (uint16_t)(w >> 16);
-  }
-}
-template <bool kVec>
-__device__ __forceinline__ void store_pair(float* p, int64_t i, float2 v, bool ok0, bool ok1) {
-  if (kVec) {
-    if (ok0) *reinterpret_cast<float2*>(p + i) = v;
-  } else {
-    if (ok0) p[i] = v.x;
-    if (ok1) p[i + 1] = v.y;
-  }
-}
-
-// Eight consecutive B or C values of one row (tokens t..t+7) for the LDS staging, kept raw in
-// registers until they are written to LDS.
-template <typename Tin> struct Raw8;
-template <> struct Raw8<uint16_t> { uint4 v; };
-template <> struct Raw8<float> { float4 a, b; };
-
-template <bool kVec>
-__device__ __forceinline__ Raw8<uint16_t> load8(const uint16_t* p, int64_t i, int64_t t,
-                                                int64_t t_end) {
-  Raw8<uint16_t> r;
-  if (kVec) {
-    r.v = (t < t_end) ? *reinterpret_cast<const uint4*>(p + i) : make_uint4(0, 0, 0, 0);
-  } else {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = (t + 2 * k < t_end) ? p[i + 2 * k] : 0u;
-      const uint32_t hi = (t + 2 * k + 1 < t_end) ? p[i + 2 * k + 1] : 0u;
-      w[k] = lo | (hi << 16);
-    }
-    r.v = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  return r;
-}
-template <bool kVec>
-__device__ __forceinline__ Raw8<float> load8(const float* p, int64_t i, int64_t t,
-                                             int64_t t_end) {
-  Raw8<float> r;
-  if (kVec) {
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    r.a = (t < t_end) ? *reinterpret_cast<const float4*>(p + i) : zero;
-    r.b = (t < t_end) ? *reinterpret_cast<const float4*>(p + i + 4) : zero;
-  } else {
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = (t + k < t_end) ? p[i + k] : 0.f;
-    r.a = make_float4(v[0], v[1], v[2], v[3]);
-    r.b = make_float4(v[4], v[5], v[6], v[7]);
-  }
-  return r;
-}
-__device__ __forceinline__ float elem8(const Raw8<uint16_t>& r, int k) {
-  const uint32_t ws = (k >> 1) == 0 ? r.v.x : (k >> 1) == 1 ? r.v.y : (k >> 1) == 2 ? r.v.z : r.v.w;
-  return (k & 1) ? __uint_as_float(ws & 0xffff0000u) : __uint_as_float(ws << 16);
-}
-__device__ __forceinline__ float elem8(const Raw8<float>& r, int k) {
-  const float4 q = k < 4 ? r.a : r.b;
-  const int j = k & 3;
-  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-}
-
-// ------------------------------------------------------------------ scalar math
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// softplus(x) = max(x, 0) + log1p(e), e = exp(-|x|) in (0, 1].  log1p(e) is ln2*log2(u) for
-// u = 1 + e (rounded) plus the rounding error d = e - (u - 1), which is exact (Sterbenz) and
-// |d| <= 2^-24: log(1+e) = log(u) + d/u + O(d^2), and using d for d/u errs by at most
-// |d|(1 - 1/u) < 3e-8 absolute, relative to log1p(e) < 6e-8.  v_log_f32 is relatively accurate
-// near 1 on gfx950 (measured 1.1e-7), so the result is accurate to ~1e-6 relative over the
-// fp32 range (dominated by the rounding of -|x|*log2(e) for large |x|).  max(x, 0) is formed as
-// (x + |x|)/2; NaN propagates; for large x, e underflows and the result is x.
-__device__ __forceinline__ float softplus_f32(float x) {
-  const float e = fast_exp2(-fabsf(x) * kLog2e);
-  const float u = 1.f + e;
-  const float d = e - (u - 1.f);
-  const float l = fmaf(__builtin_amdgcn_logf(u), kLn2, d);
-  return fmaf(0.5f, x + fabsf(x), l);
-}
-
-// silu(z) = z / (1 + exp(-z)).
-__device__ __forceinline__ float silu_f32(float z) {
-  return z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-z * kLog2e));
-}
-
-// Keeps the compiler from moving LDS accesses across this point.  Within one wavefront the
-// hardware executes LDS instructions in issue order, so this orders cross-lane exchanges
-// through LDS inside a wave.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+namespace mamba {
 
 // ------------------------------------------------------------------ scan
-
-struct ScanArgs {
-  const void* u;
-  const void* delta;
-  const float* A;
-  const void* B;
-  const void* C;
-  const float* D;
-  const void* z;
-  const float* bias;
-  void* out;
-  float* last_state;
-  float* ws_S;   // (batch*dim, nchunks-1): sum of Delta over the chunk
-  float* ws_H;   // (batch*dim, nchunks-1, 16): chunk-local final state from h = 0
-  int64_t batch, dim, L;
-  int64_t chunk_len;
-  int32_t nchunks;
-  int32_t dblocks;  // ceil(dim / kChWG)
-  int32_t softplus;
-};
 
 struct __align__(16) ScanSmem {
   float y[kWaves][kChW * 8][kYStride];   // partial readouts per lane and token (first: short
@@ -233,18 +46,22 @@ struct __align__(16) ScanSmem {
 //   lane = 8*c + g: channel c of the wave; g is the state group (states 2g, 2g+1) in the
 //   recurrence, and the token pair (2g, 2g+1 of each 16-token sub-tile) in the element-wise
 //   prologue/epilogue.
-// kMain = true: full forward of the chunk (carry-in, readout, epilogue, last_state).
-// kMain = false: chunk summary (local final state from zero and sum of Delta), no output.
+// kMode = kModeMain: full forward of the chunk (carry-in, readout, epilogue, last_state).
+// kMode = kModeSummary: chunk summary (local final state from zero and sum of Delta), no output.
+// kMode = kModeCkpt: carry-in and recurrence only; the state before every 8th token is stored
+//   (the backward pass recomputes each 8-token block from these checkpoints).
 // kVec: seqlen % 8 == 0 and 16-byte aligned tensors -> vector loads and stores.
 // kSoftplus / kGate: softplus on Delta / z gate present (compile-time, no per-element selects).
-template <typename Tin, bool kMain, bool kVec, bool kSoftplus, bool kGate>
+template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate>
 struct ScanThread {
+  static constexpr bool kMain = kMode == kModeMain;
   using Raw = typename RawPair<Tin>::T;
   ScanSmem& sm;
   const Tin* __restrict__ U;
   const Tin* __restrict__ DL;
   const Tin* __restrict__ Z;
   Tin* __restrict__ O;
+  float* __restrict__ CK;  // checkpoint row of this lane's channel, offset by 2g
   const Tin* __restrict__ BCrow;
   int w, lane, c, g, sq, sslot, sg;
   bool dvalid;
@@ -317,7 +134,7 @@ struct ScanThread {
         dl0 = ok0 ? dl0 : 0.f;
         dl1 = ok1 ? dl1 : 0.f;
       }
-      if (!kMain) dsum += dl0 + dl1;
+      if (kMode == kModeSummary) dsum += dl0 + dl1;
       sm.dd[w][2 * g][c] = make_float2(dl0, dl0 * x.x);
       sm.dd[w][2 * g + 1][c] = make_float2(dl1, dl1 * x.y);
       wave_lds_fence();
@@ -331,6 +148,11 @@ struct ScanThread {
         const float4 bc = sm.bc[kTS * s + tl][g];
         const float e0 = fast_exp2(q.x * a0);
         const float e1 = fast_exp2(q.x * a1);
+        if (kMode == kModeCkpt && (tl == 0 || tl == 8)) {
+          // state before token tb + tl (block (tb + tl) / 8); guards: block inside the sequence
+          if (dvalid && tb + tl < t_end)
+            *reinterpret_cast<float2*>(CK + ((tb + tl) >> 3) * kN) = make_float2(h0, h1);
+        }
         h0 = fmaf(e0, h0, q.y * bc.x);
         h1 = fmaf(e1, h1, q.y * bc.y);
         if (kMain) yp[tl] = fmaf(bc.w, h1, bc.z * h0);
@@ -368,10 +190,11 @@ struct ScanThread {
   }
 };
 
-template <typename Tin, bool kMain, bool kVec, bool kSoftplus, bool kGate>
+template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate>
 __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
+  constexpr bool kMain = kMode == kModeMain;
   __shared__ ScanSmem sm;
-  ScanThread<Tin, kMain, kVec, kSoftplus, kGate> th(sm);
+  ScanThread<Tin, kMode, kVec, kSoftplus, kGate> th(sm);
   th.U = static_cast<const Tin*>(p.u);
   th.DL = static_cast<const Tin*>(p.delta);
   th.Z = static_cast<const Tin*>(p.z);
@@ -396,6 +219,7 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   const int64_t dd_ = th.dvalid ? d : (cb - b * p.dblocks) * kChWG;
   const int64_t ch = b * p.dim + dd_;
   th.row = ch * p.L;
+  if (kMode == kModeCkpt) th.CK = p.ckpt + ch * p.nblk8 * kN + 2 * g;
   const int64_t t_begin = k * p.chunk_len;
   th.t_end = min(p.L, t_begin + p.chunk_len);
 
@@ -404,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   th.bias = p.bias ? p.bias[dd_] : 0.f;
   th.dskip = (kMain && p.D) ? p.D[dd_] : 0.f;
 
-  if (kMain && k > 0) {
+  if (kMode != kModeSummary && k > 0) {
     // carry-in: compose the summaries of chunks 0..k-1 in order
     const int64_t nsum = p.nchunks - 1;
     const float* S = p.ws_S + ch * nsum;
@@ -442,12 +266,12 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   for (; t0 + kTT <= t_end; t0 += kTT) th.template tile<true>(t0);
   if (t0 < t_end) th.template tile<false>(t0);
 
-  if (kMain) {
+  if (kMode == kModeMain) {
     if (p.last_state && th.dvalid && k == p.nchunks - 1) {
       p.last_state[ch * kN + 2 * g] = th.h0;
       p.last_state[ch * kN + 2 * g + 1] = th.h1;
     }
-  } else {
+  } else if (kMode == kModeSummary) {
     // sum of Delta over the chunk: reduce the 8 token-pair lanes of this channel, fixed order
     float sd = th.dsum;
     sd += __shfl_xor(sd, 1);
@@ -522,87 +346,50 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
   }
 }
 
-// ------------------------------------------------------------------ host: validation and plan
-
-struct Plan {
-  int64_t chunk_len;
-  int64_t nchunks;
-  int64_t dblocks;
-  size_t ws_bytes;
-};
-
-inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-int check_dims(const mamba_dims* dm, bool step) {
-  if (!dm) return MAMBA_ERR_NULL;
-  if (dm->io_dtype != MAMBA_F32 && dm->io_dtype != MAMBA_BF16) return MAMBA_ERR_DTYPE;
-  if (dm->batch <= 0 || dm->dim <= 0 || dm->dstate <= 0 || dm->seqlen <= 0)
-    return MAMBA_ERR_SHAPE;
-  if (dm->dstate != kN) return MAMBA_ERR_UNSUPPORTED;
-  if (step && dm->seqlen != 1) return MAMBA_ERR_SHAPE;
-  const int64_t lim = (int64_t)1 << 40;  // elements per tensor
-  if (dm->batch > lim || dm->dim > lim || dm->seqlen > lim) return MAMBA_ERR_SHAPE;
-  if ((double)dm->batch * (double)dm->dim * (double)dm->seqlen > (double)lim)
-    return MAMBA_ERR_SHAPE;
-  if (!step && (dm->chunk_len < 0 || dm->chunk_len % kChunkAlign != 0)) return MAMBA_ERR_SHAPE;
-  return MAMBA_OK;
-}
-
-int make_plan(const mamba_dims* dm, Plan* pl) {
-  const int64_t L = dm->seqlen;
-  pl->dblocks = (dm->dim + kChWG - 1) / kChWG;
-  const int64_t nwg_ch = dm->batch * pl->dblocks;
-  int64_t cl = dm->chunk_len;
-  if (cl == 0) {
-    // as many chunks as keep every workgroup of the main pass resident at once (5 per CU on
-    // 256 CUs): a second round of a few workgroups would nearly double a long pass
-    int64_t K = kTargetWG / nwg_ch;
-    const int64_t maxK = (L + kChunkAlign - 1) / kChunkAlign;
-    if (K > maxK) K = maxK;
-    if (K < 1) K = 1;
-    cl = ((L + K - 1) / K + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
-  }
-  pl->chunk_len = cl;
-  pl->nchunks = (L + cl - 1) / cl;
-  if (pl->nchunks * nwg_ch > 0x7fffffffLL) return MAMBA_ERR_SHAPE;
-  pl->ws_bytes = pl->nchunks > 1
-                     ? (size_t)(dm->batch * dm->dim) * (size_t)(pl->nchunks - 1) * (kN + 1) *
-                           sizeof(float)
-                     : 0;
-  return MAMBA_OK;
-}
-
-int launch_status() {
-  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
-}
-
-template <typename Tin, bool kMain, bool kVec, bool kSoftplus, bool kGate>
+template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate>
 int launch_one(dim3 grid, hipStream_t s, const ScanArgs& a) {
-  hipLaunchKernelGGL((scan_kernel<Tin, kMain, kVec, kSoftplus, kGate>), grid, dim3(kThreads), 0,
+  hipLaunchKernelGGL((scan_kernel<Tin, kMode, kVec, kSoftplus, kGate>), grid, dim3(kThreads), 0,
                      s, a);
   return launch_status();
 }
 
-template <typename Tin, bool kMain, bool kVec>
+template <typename Tin, int kMode, bool kVec>
 int launch_flags(bool softplus, bool gate, dim3 grid, hipStream_t s, const ScanArgs& a) {
-  if (!kMain) gate = false;  // the summary pass has no readout
+  constexpr bool kG = kMode == kModeMain;  // only the main pass has a readout to gate
   if (softplus)
-    return gate ? launch_one<Tin, kMain, kVec, true, kMain>(grid, s, a)
-                : launch_one<Tin, kMain, kVec, true, false>(grid, s, a);
-  return gate ? launch_one<Tin, kMain, kVec, false, kMain>(grid, s, a)
-              : launch_one<Tin, kMain, kVec, false, false>(grid, s, a);
+    return gate ? launch_one<Tin, kMode, kVec, true, kG>(grid, s, a)
+                : launch_one<Tin, kMode, kVec, true, false>(grid, s, a);
+  return gate ? launch_one<Tin, kMode, kVec, false, kG>(grid, s, a)
+              : launch_one<Tin, kMode, kVec, false, false>(grid, s, a);
 }
 
-template <bool kMain>
+template <int kMode>
 int launch_scan(bool bf, bool vec, bool softplus, bool gate, dim3 grid, hipStream_t s,
                 const ScanArgs& a) {
-  if (bf) return vec ? launch_flags<uint16_t, kMain, true>(softplus, gate, grid, s, a)
-                     : launch_flags<uint16_t, kMain, false>(softplus, gate, grid, s, a);
-  return vec ? launch_flags<float, kMain, true>(softplus, gate, grid, s, a)
-             : launch_flags<float, kMain, false>(softplus, gate, grid, s, a);
+  if (kMode != kModeMain) gate = false;
+  if (bf) return vec ? launch_flags<uint16_t, kMode, true>(softplus, gate, grid, s, a)
+                     : launch_flags<uint16_t, kMode, false>(softplus, gate, grid, s, a);
+  return vec ? launch_flags<float, kMode, true>(softplus, gate, grid, s, a)
+             : launch_flags<float, kMode, false>(softplus, gate, grid, s, a);
 }
 
-}  // namespace
+}  // namespace mamba
+
+int mamba::launch_fwd(int mode, bool bf, bool vec, bool softplus, bool gate, dim3 grid,
+                      hipStream_t s, const ScanArgs& a) {
+  switch (mode) {
+    case kModeSummary: return launch_scan<kModeSummary>(bf, vec, softplus, gate, grid, s, a);
+    case kModeMain: return launch_scan<kModeMain>(bf, vec, softplus, gate, grid, s, a);
+    case kModeCkpt: return launch_scan<kModeCkpt>(bf, vec, softplus, gate, grid, s, a);
+    default: return MAMBA_ERR_UNSUPPORTED;
+  }
+}
+
+namespace mamba {
+
+}  // namespace mamba
+
+using namespace mamba;
 
 extern "C" {
 
@@ -637,6 +424,8 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
   a.out = out; a.last_state = last_state;
   a.ws_S = static_cast<float*>(workspace);
   a.ws_H = pl.ws_bytes ? a.ws_S + (size_t)(dims->batch * dims->dim) * (pl.nchunks - 1) : nullptr;
+  a.ckpt = nullptr;
+  a.nblk8 = (dims->seqlen + 7) / 8;
   a.batch = dims->batch; a.dim = dims->dim; a.L = dims->seqlen;
   a.chunk_len = pl.chunk_len; a.nchunks = (int32_t)pl.nchunks; a.dblocks = (int32_t)pl.dblocks;
   a.softplus = softplus_flag ? 1 : 0;
@@ -647,11 +436,11 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
   if (pl.nchunks > 1) {
     dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
-    if (launch_scan<false>(bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
+    if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
       return MAMBA_ERR_HIP;
   }
   dim3 grid((unsigned)(nwg_ch * pl.nchunks));
-  return launch_scan<true>(bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
+  return launch_fwd(kModeMain, bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const float* A,

@@ -27,6 +27,7 @@ BLOCK_ROWS = 64
 
 # tensor ids used in the seed sequences
 _T_BIAS, _T_U, _T_DELTA, _T_Z, _T_B, _T_C, _T_STATE = 0, 1, 2, 3, 4, 5, 6
+_T_DOUT, _T_DLAST = 8, 9  # (7 is the selective-copying stream)
 
 
 @dataclass(frozen=True)
@@ -138,6 +139,19 @@ def scan_inputs(w: Workload, channels=None):
     B = _normal_rows(w.seed, _T_B, w.batch * w.dstate, L, None, bf).reshape(w.batch, w.dstate, L)
     C = _normal_rows(w.seed, _T_C, w.batch * w.dstate, L, None, bf).reshape(w.batch, w.dstate, L)
     return dict(u=u, delta=delta, z=z, B=B, C=C, A=A, D=D, delta_bias=bias)
+
+
+def grad_inputs(w: Workload, channels=None):
+    """Output gradients for the backward pass of a whole-sequence workload: dout (batch, dim, L)
+    ~ N(0, 1) in the workload's storage precision and dlast (batch, dim, N) ~ N(0, 1) fp32.
+    channels: as for scan_inputs (rows of dout and dlast only)."""
+    bf = w.io_dtype == "bf16"
+    nrows = w.batch * w.dim
+    dshape = (w.batch, w.dim, w.seqlen) if channels is None else (len(channels), w.seqlen)
+    lshape = (w.batch, w.dim, w.dstate) if channels is None else (len(channels), w.dstate)
+    dout = _normal_rows(w.seed, _T_DOUT, nrows, w.seqlen, channels, bf).reshape(dshape)
+    dlast = _normal_rows(w.seed, _T_DLAST, nrows, w.dstate, channels, False).reshape(lshape)
+    return dict(dout=dout, dlast=dlast)
 
 
 def step_inputs(w: Workload, steps=None, channels=None):

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mamba_abi_version() == 1
+    assert lib.mamba_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -100,3 +100,41 @@ def test_step_validation_codes(lib):
     assert step(dims(seqlen=1, dstate=32)) == -4
     assert step(dims(seqlen=1), state=ctypes.c_void_p(0x10004)) == -5   # state needs 16-B
     assert step(dims(seqlen=1, io=3)) == -3
+
+
+def call_bwd(lib, dm, u=FAKE, z=None, dz=None, dout=FAKE, du=FAKE, dB=FAKE, dA=FAKE, ws=FAKE,
+             ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(dm)) if dm is not None else 0
+    return lib.mamba_scan_bwd(u, FAKE, FAKE, FAKE, FAKE, None, z, None, 1, dout, None, du, FAKE,
+                              dA, dB, FAKE, None, dz, None,
+                              ctypes.byref(dm) if dm is not None else None, ws, ws_bytes, None)
+
+
+def test_bwd_validation_codes(lib):
+    assert call_bwd(lib, None) == -1
+    assert call_bwd(lib, dims(), dout=None) == -1
+    assert call_bwd(lib, dims(), du=None) == -1
+    assert call_bwd(lib, dims(), dA=None) == -1
+    assert call_bwd(lib, dims(), z=FAKE, dz=None) == -1      # a gate needs its gradient
+    assert call_bwd(lib, dims(batch=0)) == -2
+    assert call_bwd(lib, dims(dstate=8)) == -4
+    assert call_bwd(lib, dims(io=2)) == -3
+    assert call_bwd(lib, dims(chunk=8)) == -2
+    assert call_bwd(lib, dims(), dB=ODD) == -5
+    assert call_bwd(lib, dims(io=1), z=FAKE, dz=ODD) == -5
+    assert call_bwd(lib, dims(), ws=None) == -6
+    assert call_bwd(lib, dims(), ws_bytes=16) == -6
+    assert call_bwd(lib, dims(), ws=ctypes.c_void_p(0x10008)) == -5   # workspace needs 16-B
+
+
+def test_bwd_workspace_bytes(lib):
+    # (batch 2, dim 64, L 128) -> 4 workgroups per chunk, chunks of 16 tokens (K = 8):
+    # forward and adjoint chunk records, checkpoints, per-workgroup dB/dC sums, dA/dD/dbias
+    # partials, each region rounded up to 64 floats
+    r = lambda n: (n + 63) // 64 * 64
+    nch, K, L = 2 * 64, 8, 128
+    want = (r(nch * (K - 1) * 17) * 2 + r(nch * (L // 8) * 16) + r(2 * 2 * L * 32) +
+            r(2 * K * 64 * 16) + 2 * r(2 * K * 64)) * 4
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(dims())) == want
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(dims(batch=0))) == 0
