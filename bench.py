@@ -35,6 +35,14 @@ ALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 #   per channel-step: bias add 1, softplus (mul 1, exp2 2, log 2, mul 1, max/add 2) 9,
 #   Delta*u 1, skip fma 1, silu (mul 1, exp2 2, add 1, rcp 2, mul 1) 7, gate mul 1  -> 19
 ALU_OPS_PER_CHANNEL_STEP = 96 + 19
+# Backward (gradients of the scan with one recomputation of the forward), per channel-step:
+#   per state, recompute 6 (as above); adjoint: lam = dy*C + carry (1), carry = Abar*lam (1),
+#   Abar*h_prev (1), *lam (1), dA fma (1), sum lam*Abar*h*A fma (1), sum lam*B fma (1),
+#   dB term lam*Delta*u (1) and its sum over channels (1), dC term dy*h (1) and its sum (1)
+#   -> 17 x 16 = 272
+#   per channel-step: softplus 9, bias add 1, Delta*u 1, skip fma 1, gate: sigmoid 6, dy 2,
+#   dz 5, softplus' (sigmoid 6, product 1) 7, dDelta fma 1, du 2, dD 1, dbias 1  -> 37
+BWD_OPS_PER_CHANNEL_STEP = 272 + 37
 
 
 def kernel_source_hash() -> str:
@@ -197,6 +205,63 @@ def time_forward(t, torch, binding, reps, warm):
     return ms[len(ms) // 2]
 
 
+def bwd_alg_bytes(batch, dim, L, N, s_io):
+    """Bytes the backward must move: u, Delta, z, dout read and du, dDelta, dz written per
+    channel-step; B, C read and dB, dC written per (sequence, token); dlast read; A, D, bias read
+    and dA, dD, dbias written."""
+    return (batch * L * dim * 7 * s_io + batch * L * 4 * N * s_io + batch * dim * N * 4
+            + 2 * (dim * N * 4 + 2 * dim * 4))
+
+
+def bench_backward(w, torch, binding, dev, reps, warm):
+    """HIP-event time of whole mamba_scan_bwd calls (every pass: checkpoints, adjoint chunk
+    summaries when chunked, gradients, reductions) on seeded device inputs."""
+    t = device_inputs(w, dev, torch, seed=7)
+    io = t["u"].dtype
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 1000 + 8)
+    dout = torch.randn(t["u"].shape, generator=g, device=dev, dtype=torch.float32).to(io)
+    dlast = torch.randn((w.batch, w.dim, w.dstate), generator=g, device=dev)
+    ws = torch.empty(binding.mamba_scan_bwd_workspace_bytes(w.batch, w.dim, w.seqlen, io),
+                     dtype=torch.uint8, device=dev)
+    grads = {}
+
+    def call():
+        return binding.mamba_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                      t["delta_bias"], True, dout, dlast, workspace=ws,
+                                      grads=grads)
+    grads.update(call())
+    for _ in range(warm):
+        call()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    chsteps = w.batch * w.dim * w.seqlen
+    s = 2 if w.io_dtype == "bf16" else 4
+    nbytes = bwd_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s)
+    ok = all(bool(torch.isfinite(v.float()).all().item()) for v in grads.values()
+             if v is not None)
+    res = dict(workload=w.name, us=med * 1e3, us_p10=ms[len(ms) // 10] * 1e3,
+               us_p90=ms[(len(ms) * 9) // 10] * 1e3, channel_steps_per_s=chsteps / (med * 1e-3),
+               alu_achieved=chsteps * BWD_OPS_PER_CHANNEL_STEP / (med * 1e-3) / 1e12,
+               alu_frac=chsteps * BWD_OPS_PER_CHANNEL_STEP / (med * 1e-3) / ALU_PEAK_LANE_OPS,
+               ops_per_channel_step=BWD_OPS_PER_CHANNEL_STEP,
+               alg_GBps=nbytes / (med * 1e-3) / 1e9, algorithmic_bytes=nbytes,
+               workspace_bytes=ws.numel(), outputs_finite=ok, reps=reps, warmup=warm,
+               note="whole backward call, all passes; ALU roofline counts one recomputation")
+    del t, dout, dlast, ws, grads
+    torch.cuda.empty_cache()
+    return res
+
+
 def other_workloads(torch, binding, synth, dev):
     """Every other whole-sequence workload, and the sequence-length sweep (batch 1, 1536
     channels, fp32) for the linear-in-L claim."""
@@ -242,6 +307,11 @@ def main():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads and the sequence-length sweep")
     ap.add_argument("--step-steps", type=int, default=1000)
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--bwd-warmup", type=int, default=60)
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="time only the backward (for profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -269,6 +339,11 @@ def main():
         _build.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.bwd_only:
+        print(json.dumps(bench_backward(w, torch, binding, dev, args.bwd_steps,
+                                        args.bwd_warmup)), flush=True)
+        return 0
 
     x = synth.scan_inputs(w)
     io = torch.bfloat16 if bf else torch.float32
@@ -357,6 +432,8 @@ def main():
                       "p90": kern_ms[(len(kern_ms) * 9) // 10] * 1e3},
         "outputs_finite": ok,
     }
+    if not args.no_bwd:
+        rec["backward"] = bench_backward(w, torch, binding, dev, args.bwd_steps, args.bwd_warmup)
     if not args.no_step:
         del t, out
         torch.cuda.empty_cache()

@@ -77,4 +77,6 @@ def test_selective_copy_on_gpu():
             rms = math.sqrt(float(np.mean(ry * ry)))
             assert np.max(np.abs(yg - ry) / np.maximum(np.abs(ry), rms)) <= 1e-4
             errs.append(recall_error(yg[0, :, -1], vals))
+        print(f"[selective copy] gap {gap}: fixed {errs[0]:.4f} selective {errs[1]:.4f}",
+              flush=True)
         assert errs[1] < errs[0], (gap, errs)
