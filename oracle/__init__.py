@@ -60,6 +60,8 @@ def _load():
                                              dp, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
                                              dp]
             lib.ref_scan_bwd_f64.restype = None
+            lib.ref_causal_conv1d_silu_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, dp]
+            lib.ref_causal_conv1d_silu_f64.restype = None
             lib.ref_affine_scan_f64.argtypes = [dp, dp, i64, ctypes.c_double, dp]
             lib.ref_affine_scan_f64.restype = None
             lib.ref_softplus_f64.argtypes = [ctypes.c_double]
@@ -165,6 +167,31 @@ def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
                              _ptr(res["dC"]), _ptr(res["dD"]), _ptr(res["dz"]),
                              _ptr(res["ddelta_bias"]))
     return res
+
+
+def conv_silu_ref(x, w, bias=None):
+    """u = silu(causal depthwise conv1d(x) + bias) in float64 (``ref_causal_conv1d_silu_f64``).
+
+    x (batch, dim, L); w (dim, W); bias (dim,) or None.  The newest token multiplies w[:, W-1];
+    tokens before the start are zero.
+    """
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    batch, dim, L = x.shape
+    assert w.ndim == 2 and w.shape[0] == dim and w.shape[1] >= 1
+    assert bias is None or bias.shape == (dim,)
+    u = np.empty_like(x)
+    _load().ref_causal_conv1d_silu_f64(_ptr(x), _ptr(w), _ptr(bias), w.shape[1], batch, dim, L,
+                                       _ptr(u))
+    return u
+
+
+def scan_conv_ref(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                  delta_softplus=False):
+    """The fused forward's definition: u = conv_silu_ref(x, conv_w, conv_b), then scan_ref.
+    Returns (out, last_state, u)."""
+    u = conv_silu_ref(x, conv_w, conv_b)
+    out, last = scan_ref(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
+    return out, last, u
 
 
 def affine_scan_ref(a, b, h0=0.0):

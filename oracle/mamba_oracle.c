@@ -259,3 +259,30 @@ void ref_scan_bwd_f64(const double* u, const double* delta, const double* A, con
   free(pB);
   free(pC);
 }
+
+/*
+ * Short causal depthwise convolution followed by SiLU, producing the scan input u from x (the
+ * block step before the SSM: "Mamba" (elemedex), "How it works" / "State Spaces, Selectively"
+ * (papermap) ch.02, which place a short convolution and a nonlinearity before the selective SSM;
+ * the width is not on the pages and is a parameter here).  Cross-correlation with left zero
+ * padding, the newest token multiplying the last tap:
+ *     u[b,d,t] = silu(bias[d] + sum_{k=0}^{W-1} w[d,k] * x[b,d,t-(W-1)+k]),  x[.,.,t<0] = 0.
+ * Layouts: x, u (batch, dim, L); w (dim, W); bias (dim) or NULL (zero).
+ */
+void ref_causal_conv1d_silu_f64(const double* x, const double* w, const double* bias, int64_t W,
+                                int64_t batch, int64_t dim, int64_t L, double* u) {
+  const int64_t nch = batch * dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t d = ch % dim;
+    const double* xr = x + ch * L;
+    for (int64_t t = 0; t < L; ++t) {
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < W; ++k) {
+        const int64_t s = t - (W - 1) + k;
+        if (s >= 0) acc += w[d * W + k] * xr[s];
+      }
+      u[ch * L + t] = silu(acc);
+    }
+  }
+}

@@ -130,3 +130,39 @@ def test_planted_adjoint_mistake_is_caught(tmp_path, monkeypatch, name, old, new
         except AssertionError:
             failures += 1
     assert failures > 0, f"no pin catches the planted mistake {name}"
+
+
+# planted mistakes in the causal conv1d + SiLU oracle
+CONV_MUTANTS = [
+    ("conv_taps_reversed", "if (s >= 0) acc += w[d * W + k] * xr[s];",
+     "if (s >= 0) acc += w[d * W + (W - 1 - k)] * xr[s];"),
+    ("conv_bias_dropped", "double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
+    ("conv_looks_ahead", "const int64_t s = t - (W - 1) + k;", "const int64_t s = t + k;"),
+    ("conv_no_silu", "u[ch * L + t] = silu(acc);", "u[ch * L + t] = acc;"),
+    ("conv_off_by_one", "const int64_t s = t - (W - 1) + k;", "const int64_t s = t - W + k;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", CONV_MUTANTS, ids=[m[0] for m in CONV_MUTANTS])
+def test_planted_conv_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    from tests import test_oracle_conv as cv
+    so = _build_mutant(tmp_path, name, old, new)
+    real = oracle._load()
+    mut = ctypes.CDLL(so)
+    for fn in ("ref_causal_conv1d_silu_f64", "ref_scan_fwd_f64", "ref_set_threads",
+               "ref_max_threads"):
+        f = getattr(mut, fn)
+        f.argtypes = getattr(real, fn).argtypes
+        f.restype = getattr(real, fn).restype
+    monkeypatch.setattr(oracle, "_lib", mut)
+    pins = [lambda: cv.test_conv_matches_torch_conv1d(4, (2, 3, 17)),
+            lambda: cv.test_conv_matches_torch_conv1d(1, (1, 5, 2)),
+            cv.test_conv_impulse_response, cv.test_conv_is_causal,
+            cv.test_conv_width_one_is_pointwise]
+    failures = 0
+    for t in pins:
+        try:
+            t()
+        except (AssertionError, IndexError):
+            failures += 1
+    assert failures > 0, f"no pin catches the planted mistake {name}"
