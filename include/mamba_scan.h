@@ -1,11 +1,13 @@
 /*
  * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
  *
- * Three operations, all from the discrete selective state-space model:
+ * Operations, all from the discrete selective state-space model:
  *
- *   mamba_scan_fwd      the whole-sequence forward ("scan") over known tokens;
- *   mamba_state_update  one generation step for one new token per sequence;
- *   mamba_scan_bwd      the gradients of mamba_scan_fwd (training), recomputing the state.
+ *   mamba_scan_fwd       the whole-sequence forward ("scan") over known tokens;
+ *   mamba_scan_fwd_conv  the same forward with the block's short causal convolution and SiLU
+ *                        fused into the scan's load stage (u computed from x on the fly);
+ *   mamba_state_update   one generation step for one new token per sequence;
+ *   mamba_scan_bwd       the gradients of mamba_scan_fwd (training), recomputing the state.
  *
  * The model (sources by page title and section):
  *   - "Mamba" (elemedex dex entry), "How it works": h_t = Abar*h_{t-1} + Bbar*x_t, y_t = C*h_t,
@@ -48,14 +50,14 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 2
+#define MAMBA_SCAN_ABI_VERSION 3
 
 enum mamba_status {
   MAMBA_OK = 0,
   MAMBA_ERR_NULL = -1,        /* a required pointer is NULL */
   MAMBA_ERR_SHAPE = -2,       /* a dimension is <= 0, too large, or chunk_len is invalid */
   MAMBA_ERR_DTYPE = -3,       /* io_dtype is not one of enum mamba_dtype */
-  MAMBA_ERR_UNSUPPORTED = -4, /* dstate != 16 */
+  MAMBA_ERR_UNSUPPORTED = -4, /* dstate != 16, or conv_width outside 1..4 */
   MAMBA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size */
   MAMBA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes() query */
   MAMBA_ERR_HIP = -7          /* the HIP runtime rejected a launch */
@@ -99,6 +101,28 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    const float* D, const void* z, const float* delta_bias, int softplus_flag,
                    void* out, float* last_state, const mamba_dims* dims, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * mamba_scan_fwd with u = silu(causal_conv1d(x)), the short depthwise convolution and SiLU that
+ * precede the selective SSM in a Mamba block ("Mamba" (elemedex), "How it works"; "State Spaces,
+ * Selectively -- Mamba" (papermap), ch.02: a short convolution and a nonlinearity before the
+ * SSM; the width is not on the pages and is a parameter), computed inside the scan's load stage
+ * so u never round-trips through HBM:
+ *     u[b,d,t] = silu(conv_bias[d] + sum_{k<W} conv_weight[d,k] * x[b,d,t-(W-1)+k]),
+ *     x at t < 0 is zero (causal; the newest token meets the last tap, as a cross-correlation).
+ *
+ *   x                : (batch, dim, seqlen), io_dtype -- replaces u of mamba_scan_fwd
+ *   conv_weight      : (dim, conv_width) fp32, conv_width in 1..4 (MAMBA_ERR_UNSUPPORTED otherwise)
+ *   conv_bias        : (dim) fp32 or NULL (zero)
+ *   u_out            : (batch, dim, seqlen), io_dtype, or NULL: receives u (for a backward pass)
+ *   everything else  : as for mamba_scan_fwd (same workspace query)
+ */
+int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
+                        int conv_width, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* delta_bias,
+                        int softplus_flag, void* out, float* last_state, void* u_out,
+                        const mamba_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * One generation step for `batch` sequences: the state is read and updated in place and one

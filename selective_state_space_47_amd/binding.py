@@ -29,7 +29,8 @@ class mamba_dims(ctypes.Structure):
                 ("chunk_len", ctypes.c_int32)]
 
 
-EXPORTS = ("mamba_scan_fwd", "mamba_state_update", "mamba_scan_workspace_bytes",
+EXPORTS = ("mamba_scan_fwd", "mamba_scan_fwd_conv", "mamba_state_update",
+           "mamba_scan_workspace_bytes",
            "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_status_string",
            "mamba_abi_version")
 
@@ -54,6 +55,10 @@ def lib():
             L.mamba_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp, fp, dp,
                                          vp, ctypes.c_size_t, vp]
             L.mamba_scan_fwd.restype = ctypes.c_int
+            L.mamba_scan_fwd_conv.argtypes = [vp, fp, fp, ctypes.c_int, vp, fp, vp, vp, fp, vp,
+                                              fp, ctypes.c_int, vp, fp, vp, dp, vp,
+                                              ctypes.c_size_t, vp]
+            L.mamba_scan_fwd_conv.restype = ctypes.c_int
             L.mamba_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp,
                                              dp, vp]
             L.mamba_state_update.restype = ctypes.c_int
@@ -168,6 +173,65 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
                            _ptr(last_state), ctypes.byref(dm), ws_ptr, ws_len, stream)
     _raise(st)
     return (out, last_state) if return_last_state else out
+
+
+def mamba_scan_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=None,
+                        delta_softplus=False, conv_bias=None, return_last_state=False,
+                        return_u=False, chunk_len=0, out=None, last_state=None, u_out=None,
+                        workspace=None):
+    """Forward with the causal conv1d + SiLU fused into the load stage (mamba_scan_fwd_conv in
+    include/mamba_scan.h).  x: (batch, dim, L) like u of mamba_scan_fwd; conv_weight: (dim, W)
+    float32, W in 1..4; conv_bias: (dim,) float32 or None.  Returns out, plus last_state and/or
+    u when requested, in that order."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, seqlen)")
+    batch, dim, L = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io = x.dtype
+    code = _io_code(io)
+    if conv_weight is None or conv_weight.dim() != 2:
+        raise ValueError("conv_weight must be (dim, width)")
+    width = conv_weight.shape[1]
+    _check(x, "x", (batch, dim, L), io, dev)
+    _check(conv_weight, "conv_weight", (dim, width), torch.float32, dev)
+    _check(conv_bias, "conv_bias", (dim,), torch.float32, dev)
+    _check(delta, "delta", (batch, dim, L), io, dev)
+    _check(z, "z", (batch, dim, L), io, dev)
+    _check(B, "B", (batch, DSTATE, L), io, dev)
+    _check(C, "C", (batch, DSTATE, L), io, dev)
+    _check(A, "A", (dim, DSTATE), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _check(out, "out", (batch, dim, L), io, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, DSTATE), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, dim, DSTATE), torch.float32, dev)
+    if return_u and u_out is None:
+        u_out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _check(u_out, "u_out", (batch, dim, L), io, dev)
+    dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+    L_ = lib()
+    ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = L_.mamba_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(width),
+                                _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
+                                _ptr(last_state), _ptr(u_out), ctypes.byref(dm),
+                                _ptr(workspace), ws_len, stream)
+    _raise(st)
+    res = [out]
+    if return_last_state:
+        res.append(last_state)
+    if return_u:
+        res.append(u_out)
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def mamba_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -172,6 +172,13 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Value of another lane of the same 16-lane row (DPP; kCtrl: row_shr:N = 0x110+N, row_ror:N =
+// 0x120+N).  Lanes without a source in the row read 0.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
+}
+
 // ------------------------------------------------------------------ forward launch arguments
 
 struct ScanArgs {
@@ -188,6 +195,10 @@ struct ScanArgs {
   float* ws_S;   // (batch*dim, nchunks-1): sum of Delta over the chunk
   float* ws_H;   // (batch*dim, nchunks-1, 16): chunk-local final state from h = 0
   float* ckpt;   // (batch*dim, ceil(L/8), 16): state before token 8j (checkpoint mode only)
+  const float* conv_w;  // (dim, conv_width) taps of the fused causal conv; NULL: u is the input
+  const float* conv_b;  // (dim) conv bias or NULL
+  void* u_out;          // optional (batch, dim, L) store of the conv output u
+  int32_t conv_width;   // 1..4
   int64_t batch, dim, L;
   int64_t chunk_len;
   int64_t nblk8;  // ceil(L / 8)

@@ -52,7 +52,9 @@ struct __align__(16) ScanSmem {
 //   (the backward pass recomputes each 8-token block from these checkpoints).
 // kVec: seqlen % 8 == 0 and 16-byte aligned tensors -> vector loads and stores.
 // kSoftplus / kGate: softplus on Delta / z gate present (compile-time, no per-element selects).
-template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate>
+// kConv: the loaded input is x and u = silu(causal depthwise conv1d(x) + bias) is formed in the
+//   prologue (width <= 4; narrower kernels are zero-padded at the oldest taps).
+template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate, bool kConv>
 struct ScanThread {
   static constexpr bool kMain = kMode == kModeMain;
   using Raw = typename RawPair<Tin>::T;
@@ -68,6 +70,9 @@ struct ScanThread {
   int64_t row, t_end;
   float a0, a1, bias, dskip;
   float h0 = 0.f, h1 = 0.f, dsum = 0.f;
+  float cw0, cw1, cw2, cw3, cbias;  // conv taps, oldest first, and bias (kConv)
+  float px0 = 0.f, px1 = 0.f;       // x of this lane's token pair in the previous sub-tile
+  Tin* __restrict__ UO;             // optional store of u (kConv, main pass)
   Raw ru[kSub], rd[kSub], rz[kSub];
   Raw8<Tin> rbc;
 
@@ -97,6 +102,25 @@ struct ScanThread {
     else if (tn < t_end) load_sub<false>(tn + kTS * s, s);
   }
 
+  // u for this lane's token pair (2g, 2g+1) from x: the window x_{2g-3..2g+1} comes from lanes
+  // g-1 and g-2 of the channel (DPP row shifts; a channel's 8 lanes are 8-aligned inside a
+  // 16-lane row) and, for g < 2, from the previous sub-tile's pairs of lanes 6 and 7 (DPP row
+  // rotations).  The conv is a cross-correlation: the newest token meets the last tap.
+  __device__ __forceinline__ float2 conv_pair(float2 xv) {
+    const float a0 = dpp_row<0x111>(xv.x), a1 = dpp_row<0x111>(xv.y);  // row_shr:1 -> lane g-1
+    const float b1 = dpp_row<0x112>(xv.y);                             // row_shr:2 -> lane g-2
+    const float p0 = dpp_row<0x129>(px0), p1 = dpp_row<0x129>(px1);    // row_ror:9: g=0 <- 7
+    const float q1 = dpp_row<0x12A>(px1);                              // row_ror:10: 0<-6, 1<-7
+    const float xm1 = g >= 1 ? a1 : p1;  // x_{2g-1}
+    const float xm2 = g >= 1 ? a0 : p0;  // x_{2g-2}
+    const float xm3 = g >= 2 ? b1 : q1;  // x_{2g-3}
+    px0 = xv.x;
+    px1 = xv.y;
+    const float s0 = fmaf(cw3, xv.x, fmaf(cw2, xm1, fmaf(cw1, xm2, fmaf(cw0, xm3, cbias))));
+    const float s1 = fmaf(cw3, xv.y, fmaf(cw2, xv.x, fmaf(cw1, xm1, fmaf(cw0, xm2, cbias))));
+    return make_float2(silu_f32(s0), silu_f32(s1));
+  }
+
   // One 64-token tile starting at t0 (kFull: all of it inside the chunk); prefetches the tile
   // starting at t0 + kTT when that starts before t_end.
   template <bool kFull>
@@ -120,7 +144,11 @@ struct ScanThread {
         ok1 = 2 * g + 1 < rem;
       }
       // ---- prologue: Delta = softplus(raw + bias), Delta*u for the lane's two tokens
-      const float2 x = unpack(ru[s]);
+      float2 x = unpack(ru[s]);
+      if (kConv) {
+        x = conv_pair(x);
+        if (kMain && UO) store_pair<kVec>(UO, row + tp, x, dvalid && ok0, dvalid && ok1);
+      }
       const float2 dr = unpack(rd[s]);
       float2 zz;
       if (kGate) zz = unpack(rz[s]);
@@ -190,11 +218,11 @@ struct ScanThread {
   }
 };
 
-template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate>
+template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate, bool kConv>
 __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   constexpr bool kMain = kMode == kModeMain;
   __shared__ ScanSmem sm;
-  ScanThread<Tin, kMode, kVec, kSoftplus, kGate> th(sm);
+  ScanThread<Tin, kMode, kVec, kSoftplus, kGate, kConv> th(sm);
   th.U = static_cast<const Tin*>(p.u);
   th.DL = static_cast<const Tin*>(p.delta);
   th.Z = static_cast<const Tin*>(p.z);
@@ -227,6 +255,23 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   th.a1 = p.A[dd_ * kN + 2 * g + 1] * kLog2e;
   th.bias = p.bias ? p.bias[dd_] : 0.f;
   th.dskip = (kMain && p.D) ? p.D[dd_] : 0.f;
+  if (kConv) {
+    // taps zero-padded at the oldest end to width 4
+    const int W = p.conv_width;
+    const float* wr = p.conv_w + dd_ * W;
+    th.cw0 = W >= 4 ? wr[W - 4] : 0.f;
+    th.cw1 = W >= 3 ? wr[W - 3] : 0.f;
+    th.cw2 = W >= 2 ? wr[W - 2] : 0.f;
+    th.cw3 = wr[W - 1];
+    th.cbias = p.conv_b ? p.conv_b[dd_] : 0.f;
+    th.UO = static_cast<Tin*>(p.u_out);
+    // the last pair of each lane in the 16 tokens before the chunk (zero before the sequence)
+    if (t_begin >= kTS) {
+      const float2 v = unpack(load_pair<kVec>(th.U, th.row + t_begin - kTS + 2 * g, true, true));
+      th.px0 = v.x;
+      th.px1 = v.y;
+    }
+  }
 
   if (kMode != kModeSummary && k > 0) {
     // carry-in: compose the summaries of chunks 0..k-1 in order
@@ -346,46 +391,105 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
   }
 }
 
-template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate>
+template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate, bool kConv>
 int launch_one(dim3 grid, hipStream_t s, const ScanArgs& a) {
-  hipLaunchKernelGGL((scan_kernel<Tin, kMode, kVec, kSoftplus, kGate>), grid, dim3(kThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((scan_kernel<Tin, kMode, kVec, kSoftplus, kGate, kConv>), grid,
+                     dim3(kThreads), 0, s, a);
   return launch_status();
 }
 
-template <typename Tin, int kMode, bool kVec>
+template <typename Tin, int kMode, bool kVec, bool kConv>
 int launch_flags(bool softplus, bool gate, dim3 grid, hipStream_t s, const ScanArgs& a) {
   constexpr bool kG = kMode == kModeMain;  // only the main pass has a readout to gate
   if (softplus)
-    return gate ? launch_one<Tin, kMode, kVec, true, kG>(grid, s, a)
-                : launch_one<Tin, kMode, kVec, true, false>(grid, s, a);
-  return gate ? launch_one<Tin, kMode, kVec, false, kG>(grid, s, a)
-              : launch_one<Tin, kMode, kVec, false, false>(grid, s, a);
+    return gate ? launch_one<Tin, kMode, kVec, true, kG, kConv>(grid, s, a)
+                : launch_one<Tin, kMode, kVec, true, false, kConv>(grid, s, a);
+  return gate ? launch_one<Tin, kMode, kVec, false, kG, kConv>(grid, s, a)
+              : launch_one<Tin, kMode, kVec, false, false, kConv>(grid, s, a);
 }
 
-template <int kMode>
+template <int kMode, bool kConv>
 int launch_scan(bool bf, bool vec, bool softplus, bool gate, dim3 grid, hipStream_t s,
                 const ScanArgs& a) {
   if (kMode != kModeMain) gate = false;
-  if (bf) return vec ? launch_flags<uint16_t, kMode, true>(softplus, gate, grid, s, a)
-                     : launch_flags<uint16_t, kMode, false>(softplus, gate, grid, s, a);
-  return vec ? launch_flags<float, kMode, true>(softplus, gate, grid, s, a)
-             : launch_flags<float, kMode, false>(softplus, gate, grid, s, a);
+  if (bf) return vec ? launch_flags<uint16_t, kMode, true, kConv>(softplus, gate, grid, s, a)
+                     : launch_flags<uint16_t, kMode, false, kConv>(softplus, gate, grid, s, a);
+  return vec ? launch_flags<float, kMode, true, kConv>(softplus, gate, grid, s, a)
+             : launch_flags<float, kMode, false, kConv>(softplus, gate, grid, s, a);
 }
 
 }  // namespace mamba
 
 int mamba::launch_fwd(int mode, bool bf, bool vec, bool softplus, bool gate, dim3 grid,
                       hipStream_t s, const ScanArgs& a) {
+  const bool conv = a.conv_w != nullptr;
   switch (mode) {
-    case kModeSummary: return launch_scan<kModeSummary>(bf, vec, softplus, gate, grid, s, a);
-    case kModeMain: return launch_scan<kModeMain>(bf, vec, softplus, gate, grid, s, a);
-    case kModeCkpt: return launch_scan<kModeCkpt>(bf, vec, softplus, gate, grid, s, a);
+    case kModeSummary:
+      return conv ? launch_scan<kModeSummary, true>(bf, vec, softplus, gate, grid, s, a)
+                  : launch_scan<kModeSummary, false>(bf, vec, softplus, gate, grid, s, a);
+    case kModeMain:
+      return conv ? launch_scan<kModeMain, true>(bf, vec, softplus, gate, grid, s, a)
+                  : launch_scan<kModeMain, false>(bf, vec, softplus, gate, grid, s, a);
+    case kModeCkpt:
+      return conv ? MAMBA_ERR_UNSUPPORTED
+                  : launch_scan<kModeCkpt, false>(bf, vec, softplus, gate, grid, s, a);
     default: return MAMBA_ERR_UNSUPPORTED;
   }
 }
 
 namespace mamba {
+
+// Forward, optionally with the fused conv (conv_w != NULL: `u` holds x).
+int scan_forward(const void* u, const float* conv_w, const float* conv_b, int conv_width,
+                 void* u_out, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                 void* out, float* last_state, const mamba_dims* dims, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims, false);
+  if (st != MAMBA_OK) return st;
+  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL;
+  const size_t es = dims->io_dtype == MAMBA_BF16 ? 2 : 4;
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
+      !aligned(out, es) || (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || (last_state && !aligned(last_state, 4)) ||
+      (conv_w && !aligned(conv_w, 4)) || (conv_b && !aligned(conv_b, 4)) ||
+      (u_out && !aligned(u_out, es)))
+    return MAMBA_ERR_ALIGN;
+  Plan pl;
+  st = make_plan(dims, &pl);
+  if (st != MAMBA_OK) return st;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
+    return MAMBA_ERR_WORKSPACE;
+  if (pl.ws_bytes > 0 && !aligned(workspace, 4)) return MAMBA_ERR_ALIGN;
+
+  ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.out = out; a.last_state = last_state;
+  a.ws_S = static_cast<float*>(workspace);
+  a.ws_H = pl.ws_bytes ? a.ws_S + (size_t)(dims->batch * dims->dim) * (pl.nchunks - 1) : nullptr;
+  a.ckpt = nullptr;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.u_out = conv_w ? u_out : nullptr;
+  a.conv_width = conv_w ? conv_width : 0;
+  a.nblk8 = (dims->seqlen + 7) / 8;
+  a.batch = dims->batch; a.dim = dims->dim; a.L = dims->seqlen;
+  a.chunk_len = pl.chunk_len; a.nchunks = (int32_t)pl.nchunks; a.dblocks = (int32_t)pl.dblocks;
+  a.softplus = softplus_flag ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nwg_ch = dims->batch * pl.dblocks;
+  const bool bf = dims->io_dtype == MAMBA_BF16;
+  const bool vec = dims->seqlen % 8 == 0 && aligned(u, 16) && aligned(delta, 16) &&
+                   aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16)) &&
+                   (!a.u_out || aligned(a.u_out, 16));
+  if (pl.nchunks > 1) {
+    dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
+    if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
+      return MAMBA_ERR_HIP;
+  }
+  dim3 grid((unsigned)(nwg_ch * pl.nchunks));
+  return launch_fwd(kModeMain, bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
+}
 
 }  // namespace mamba
 
@@ -404,43 +508,21 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    const float* D, const void* z, const float* delta_bias, int softplus_flag,
                    void* out, float* last_state, const mamba_dims* dims, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  int st = check_dims(dims, false);
-  if (st != MAMBA_OK) return st;
-  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL;
-  const size_t es = dims->io_dtype == MAMBA_BF16 ? 2 : 4;
-  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
-      !aligned(out, es) || (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
-      (delta_bias && !aligned(delta_bias, 4)) || (last_state && !aligned(last_state, 4)))
-    return MAMBA_ERR_ALIGN;
-  Plan pl;
-  st = make_plan(dims, &pl);
-  if (st != MAMBA_OK) return st;
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
-    return MAMBA_ERR_WORKSPACE;
-  if (pl.ws_bytes > 0 && !aligned(workspace, 4)) return MAMBA_ERR_ALIGN;
+  return scan_forward(u, nullptr, nullptr, 0, nullptr, delta, A, B, C, D, z, delta_bias,
+                      softplus_flag, out, last_state, dims, workspace, workspace_bytes, stream);
+}
 
-  ScanArgs a;
-  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-  a.out = out; a.last_state = last_state;
-  a.ws_S = static_cast<float*>(workspace);
-  a.ws_H = pl.ws_bytes ? a.ws_S + (size_t)(dims->batch * dims->dim) * (pl.nchunks - 1) : nullptr;
-  a.ckpt = nullptr;
-  a.nblk8 = (dims->seqlen + 7) / 8;
-  a.batch = dims->batch; a.dim = dims->dim; a.L = dims->seqlen;
-  a.chunk_len = pl.chunk_len; a.nchunks = (int32_t)pl.nchunks; a.dblocks = (int32_t)pl.dblocks;
-  a.softplus = softplus_flag ? 1 : 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nwg_ch = dims->batch * pl.dblocks;
-  const bool bf = dims->io_dtype == MAMBA_BF16;
-  const bool vec = dims->seqlen % 8 == 0 && aligned(u, 16) && aligned(delta, 16) &&
-                   aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
-  if (pl.nchunks > 1) {
-    dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
-    if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
-      return MAMBA_ERR_HIP;
-  }
-  dim3 grid((unsigned)(nwg_ch * pl.nchunks));
-  return launch_fwd(kModeMain, bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
+int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
+                        int conv_width, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* delta_bias,
+                        int softplus_flag, void* out, float* last_state, void* u_out,
+                        const mamba_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!conv_weight) return MAMBA_ERR_NULL;
+  if (conv_width < 1 || conv_width > 4) return MAMBA_ERR_UNSUPPORTED;
+  return scan_forward(x, conv_weight, conv_bias, conv_width, u_out, delta, A, B, C, D, z,
+                      delta_bias, softplus_flag, out, last_state, dims, workspace,
+                      workspace_bytes, stream);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const float* A,

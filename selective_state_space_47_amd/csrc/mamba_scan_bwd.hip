@@ -473,6 +473,10 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   f.ws_S = pl.nchunks > 1 ? ws + lay.fwd_sum : nullptr;
   f.ws_H = pl.nchunks > 1 ? f.ws_S + nch * (pl.nchunks - 1) : nullptr;
   f.ckpt = ws + lay.ckpt;
+  f.conv_w = nullptr;
+  f.conv_b = nullptr;
+  f.u_out = nullptr;
+  f.conv_width = 0;
   f.batch = dims->batch; f.dim = dims->dim; f.L = dims->seqlen;
   f.chunk_len = pl.chunk_len; f.nblk8 = (dims->seqlen + kBT - 1) / kBT;
   f.nchunks = (int32_t)pl.nchunks; f.dblocks = (int32_t)pl.dblocks; f.softplus = sp ? 1 : 0;

@@ -28,6 +28,7 @@ BLOCK_ROWS = 64
 # tensor ids used in the seed sequences
 _T_BIAS, _T_U, _T_DELTA, _T_Z, _T_B, _T_C, _T_STATE = 0, 1, 2, 3, 4, 5, 6
 _T_DOUT, _T_DLAST = 8, 9  # (7 is the selective-copying stream)
+_T_CONV = 10
 
 
 @dataclass(frozen=True)
@@ -152,6 +153,16 @@ def grad_inputs(w: Workload, channels=None):
     dout = _normal_rows(w.seed, _T_DOUT, nrows, w.seqlen, channels, bf).reshape(dshape)
     dlast = _normal_rows(w.seed, _T_DLAST, nrows, w.dstate, channels, False).reshape(lshape)
     return dict(dout=dout, dlast=dlast)
+
+
+def conv_params(w: Workload, width: int = 4):
+    """Depthwise causal-conv taps (dim, width) and bias (dim,), fp32, uniform in
+    [-1/sqrt(width), 1/sqrt(width)] (the usual fan-in scaling of a depthwise convolution)."""
+    r = _rng(w.seed, _T_CONV, width)
+    bound = 1.0 / np.sqrt(width)
+    taps = r.uniform(-bound, bound, size=(w.dim, width)).astype(np.float32)
+    bias = r.uniform(-bound, bound, size=w.dim).astype(np.float32)
+    return taps, bias
 
 
 def step_inputs(w: Workload, steps=None, channels=None):

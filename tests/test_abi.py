@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mamba_abi_version() == 2
+    assert lib.mamba_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -138,3 +138,19 @@ def test_bwd_workspace_bytes(lib):
             r(2 * K * 64 * 16) + 2 * r(2 * K * 64)) * 4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(dims())) == want
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(dims(batch=0))) == 0
+
+
+def test_conv_validation_codes(lib):
+    def conv(dm, x=FAKE, w=FAKE, width=4, u_out=None):
+        return lib.mamba_scan_fwd_conv(x, w, None, width, FAKE, FAKE, FAKE, FAKE, None, None,
+                                       None, 1, FAKE, None, u_out,
+                                       ctypes.byref(dm) if dm is not None else None, None, 0,
+                                       None)
+    dm = dims(batch=1, dim=64, seqlen=128)
+    assert conv(dm, w=None) == -1
+    assert conv(dm, width=0) == -4
+    assert conv(dm, width=5) == -4
+    assert conv(None) == -1
+    assert conv(dm, x=None) == -1
+    assert conv(dm, u_out=ODD) == -5
+    assert conv(dims(batch=1, dim=64, seqlen=128, chunk=8)) == -2
