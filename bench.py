@@ -43,6 +43,9 @@ ALU_OPS_PER_CHANNEL_STEP = 96 + 19
 #   per channel-step: softplus 9, bias add 1, Delta*u 1, skip fma 1, gate: sigmoid 6, dy 2,
 #   dz 5, softplus' (sigmoid 6, product 1) 7, dDelta fma 1, du 2, dD 1, dbias 1  -> 37
 BWD_OPS_PER_CHANNEL_STEP = 272 + 37
+# Forward with the fused causal conv (width 4) + SiLU: the forward's 115 plus 4 fma (taps + bias
+# as the first fma's addend) and silu 7 -> 126
+CONV_OPS_PER_CHANNEL_STEP = ALU_OPS_PER_CHANNEL_STEP + 4 + 7
 
 
 def kernel_source_hash() -> str:
@@ -262,6 +265,44 @@ def bench_backward(w, torch, binding, dev, reps, warm):
     return res
 
 
+def bench_conv(w, torch, binding, synth, dev, reps, warm, plain_us):
+    """HIP-event time of whole mamba_scan_fwd_conv calls (width 4, u not stored) on seeded device
+    inputs: x takes the place of u, so the HBM bytes equal the plain forward's."""
+    t = device_inputs(w, dev, torch, seed=9)
+    cw, cb = synth.conv_params(w, 4)
+    cw, cb = torch.from_numpy(cw).to(dev), torch.from_numpy(cb).to(dev)
+    out = torch.empty_like(t["u"])
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def call():
+        binding.mamba_scan_fwd_conv(t["u"], cw, t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                    t["z"], t["delta_bias"], True, conv_bias=cb,
+                                    return_last_state=True, out=out, last_state=last)
+    for _ in range(warm):
+        call()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    chsteps = w.batch * w.dim * w.seqlen
+    ok = bool(torch.isfinite(out.float()).all().item())
+    del t, out, last
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, conv_width=4, us=med * 1e3, us_p10=ms[len(ms) // 10] * 1e3,
+                us_p90=ms[(len(ms) * 9) // 10] * 1e3, channel_steps_per_s=chsteps / (med * 1e-3),
+                alu_frac=chsteps * CONV_OPS_PER_CHANNEL_STEP / (med * 1e-3) / ALU_PEAK_LANE_OPS,
+                ops_per_channel_step=CONV_OPS_PER_CHANNEL_STEP,
+                overhead_vs_plain_forward=med * 1e3 / plain_us - 1.0, outputs_finite=ok,
+                reps=reps, warmup=warm)
+
+
 def other_workloads(torch, binding, synth, dev):
     """Every other whole-sequence workload, and the sequence-length sweep (batch 1, 1536
     channels, fp32) for the linear-in-L claim."""
@@ -308,6 +349,7 @@ def main():
                     help="skip the other workloads and the sequence-length sweep")
     ap.add_argument("--step-steps", type=int, default=1000)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-conv", action="store_true", help="skip the fused-conv forward timing")
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--bwd-warmup", type=int, default=60)
     ap.add_argument("--bwd-only", action="store_true",
@@ -432,6 +474,9 @@ def main():
                       "p90": kern_ms[(len(kern_ms) * 9) // 10] * 1e3},
         "outputs_finite": ok,
     }
+    if not args.no_conv:
+        rec["conv_fused_forward"] = bench_conv(w, torch, binding, synth, dev, 30, 100,
+                                               kern_ms[len(kern_ms) // 2] * 1e3)
     if not args.no_bwd:
         rec["backward"] = bench_backward(w, torch, binding, dev, args.bwd_steps, args.bwd_warmup)
     if not args.no_step:
