@@ -185,6 +185,25 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
                    const mamba_dims* dims, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * Batched bf16 matrix product on the matrix cores, for the learned projections of a Mamba block
+ * ("Mamba" (visual-learn), "Simplifications and limits": a real block adds learned projections;
+ * "Mamba" (elemedex), "How it works": the block starts with a linear projection):
+ *     C[b] (M x N) = A (M x K) * B[b] (K x N),  fp32 accumulation, bf16 output (RNE).
+ *   A : row-major, element (m, k) at A[m*lda + k], lda >= K; shared by every b
+ *   B : b_kcontig != 0: element (k, n) at B[b*b_bstride + n*ldb + k] (ldb >= K);
+ *       b_kcontig == 0: element (k, n) at B[b*b_bstride + k*ldb + n] (ldb >= N)
+ *   C : c_trans == 0: element (m, n) at C[b*c_bstride + m*ldc + n] (ldc >= N);
+ *       c_trans != 0: element (m, n) at C[b*c_bstride + n*ldc + m] (ldc >= M, ldc % 4 == 0,
+ *       C 8-byte aligned)
+ * A, B and C hold bf16 values (16-bit storage).  Requirements (MAMBA_ERR_SHAPE / _ALIGN otherwise):
+ * M % 16 == 0, N % 8 == 0, K % 8 == 0, lda and ldb multiples of 8, A and B 16-byte aligned,
+ * 1 <= batch <= 65535.  C must not overlap A or B.
+ */
+int mamba_gemm_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                    int64_t batch, int64_t lda, int64_t ldb, int64_t b_bstride, int64_t ldc,
+                    int64_t c_bstride, int b_kcontig, int c_trans, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* mamba_status_string(int status);
 

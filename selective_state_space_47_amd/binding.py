@@ -31,8 +31,8 @@ class mamba_dims(ctypes.Structure):
 
 EXPORTS = ("mamba_scan_fwd", "mamba_scan_fwd_conv", "mamba_state_update",
            "mamba_scan_workspace_bytes",
-           "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_status_string",
-           "mamba_abi_version")
+           "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_gemm_bf16",
+           "mamba_status_string", "mamba_abi_version")
 
 
 def library_path() -> str:
@@ -70,6 +70,10 @@ def lib():
             L.mamba_scan_bwd.restype = ctypes.c_int
             L.mamba_scan_bwd_workspace_bytes.argtypes = [dp]
             L.mamba_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+            i64 = ctypes.c_int64
+            L.mamba_gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
+                                          i64, ctypes.c_int, ctypes.c_int, vp]
+            L.mamba_gemm_bf16.restype = ctypes.c_int
             L.mamba_status_string.argtypes = [ctypes.c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             L.mamba_abi_version.argtypes = []
@@ -335,3 +339,30 @@ def mamba_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
                            ctypes.byref(dm), _ptr(workspace), ws_len, stream)
     _raise(st)
     return {k: g[k] for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias")}
+
+
+def mamba_gemm_bf16(A, B, b_kcontig=True, c_trans=False, out=None):
+    """Batched bf16 GEMM on the matrix cores (mamba_gemm_bf16 in include/mamba_scan.h).
+
+    A: (M, K) bfloat16.  B: (batch, N, K) when b_kcontig (element (k, n) = B[b, n, k]), else
+    (batch, K, N).  Returns C: (batch, M, N), or (batch, N, M) when c_trans, bfloat16.
+    """
+    if A.dim() != 2 or B.dim() != 3:
+        raise ValueError("A must be (M, K) and B (batch, N, K) or (batch, K, N)")
+    M, K = A.shape
+    batch = B.shape[0]
+    N = B.shape[1] if b_kcontig else B.shape[2]
+    dev = A.device
+    _check(A, "A", (M, K), torch.bfloat16, dev)
+    _check(B, "B", (batch, N, K) if b_kcontig else (batch, K, N), torch.bfloat16, dev)
+    shape = (batch, N, M) if c_trans else (batch, M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", shape, torch.bfloat16, dev)
+    ldb = K if b_kcontig else N
+    ldc = M if c_trans else N
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = lib().mamba_gemm_bf16(_ptr(A), _ptr(B), _ptr(out), M, N, K, batch, K, ldb, N * K,
+                               ldc, M * N, int(bool(b_kcontig)), int(bool(c_trans)), stream)
+    _raise(st)
+    return out

@@ -22,7 +22,7 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
