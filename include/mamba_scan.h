@@ -204,6 +204,46 @@ int mamba_gemm_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                     int64_t batch, int64_t lda, int64_t ldb, int64_t b_bstride, int64_t ldc,
                     int64_t c_bstride, int b_kcontig, int c_trans, void* stream);
 
+/* Sizes of a Mamba block (mamba_block_fwd). */
+typedef struct mamba_block_dims {
+  int64_t batch;      /* sequences, 1..65535 */
+  int64_t seqlen;     /* tokens L, a multiple of 8 */
+  int64_t d_model;    /* width of the block's input and output, a multiple of 16 */
+  int64_t d_inner;    /* channels E of the scan, a multiple of 16 */
+  int64_t dstate;     /* N, must be 16 */
+  int64_t dt_rank;    /* R, rank of the Delta projection, a multiple of 16 */
+  int32_t conv_width; /* 1..4 */
+  int32_t reserved;   /* set to 0 */
+} mamba_block_dims;
+
+/* Bytes of device workspace mamba_block_fwd needs (0 for invalid dims): the bf16 intermediates
+ * x, z, u, Delta_raw, y (5 x batch*E*L), Delta_low, B, C and the scan's chunk records. */
+size_t mamba_block_workspace_bytes(const mamba_block_dims* dims);
+
+/*
+ * A whole Mamba block forward with caller-supplied (e.g. random) weights, sources: "Mamba"
+ * (elemedex), "How it works" (linear projection, short convolution, selective SSM, multiplicative
+ * gate); "State Spaces, Selectively -- Mamba" (papermap), ch.02 (Delta, B, C computed from the
+ * token); "Mamba" (visual-learn), "Simplifications and limits" (learned projections, short
+ * convolution, output gate).  Per sequence, with E = d_inner, R = dt_rank, N = dstate:
+ *     [x; z]          = W_in hidden^T                      W_in  (2E, d_model) bf16
+ *     u               = silu(causal_conv1d(x) + conv_bias)  conv_weight (E, conv_width) fp32
+ *     [dlow; B; C]    = W_x u                               W_x   (R + 2N, E) bf16
+ *     Delta_raw       = W_dt dlow                           W_dt  (E, R) bf16
+ *     y               = scan(u, Delta_raw, A, B, C, D, z, dt_bias, softplus)   (mamba_scan_fwd)
+ *     out             = (W_out y)^T                         W_out (d_model, E) bf16
+ *   hidden, out : (batch, seqlen, d_model) bf16, token-major; out 8-byte aligned
+ *   A           : (E, N) fp32; D, dt_bias, conv_bias: (E) fp32 or NULL (zero)
+ * The projections run as bf16 MFMA GEMMs with fp32 accumulation; intermediates are stored in
+ * bf16 in the workspace (>= mamba_block_workspace_bytes, 256-byte aligned).  Weight matrices and
+ * hidden must be 16-byte aligned, A 16-byte aligned.
+ */
+int mamba_block_fwd(const void* hidden, const void* w_in, const float* conv_weight,
+                    const float* conv_bias, const void* w_x, const void* w_dt,
+                    const float* dt_bias, const float* A, const float* D, const void* w_out,
+                    void* out, const mamba_block_dims* dims, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* mamba_status_string(int status);
 

@@ -10,7 +10,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmamba_scan.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("mamba_scan.hip", "mamba_scan_bwd.hip", "mamba_gemm.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("mamba_scan.hip", "mamba_scan_bwd.hip", "mamba_gemm.hip",
+                                                 "mamba_block.hip")]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

@@ -23,6 +23,13 @@ _lock = threading.Lock()
 _LIB = None
 
 
+class mamba_block_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("d_model", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("dt_rank", ctypes.c_int64),
+                ("conv_width", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class mamba_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
                 ("seqlen", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
@@ -32,7 +39,8 @@ class mamba_dims(ctypes.Structure):
 EXPORTS = ("mamba_scan_fwd", "mamba_scan_fwd_conv", "mamba_state_update",
            "mamba_scan_workspace_bytes",
            "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_gemm_bf16",
-           "mamba_status_string", "mamba_abi_version")
+           "mamba_block_fwd", "mamba_block_workspace_bytes", "mamba_status_string",
+           "mamba_abi_version")
 
 
 def library_path() -> str:
@@ -74,6 +82,12 @@ def lib():
             L.mamba_gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64,
                                           i64, ctypes.c_int, ctypes.c_int, vp]
             L.mamba_gemm_bf16.restype = ctypes.c_int
+            bp = ctypes.POINTER(mamba_block_dims)
+            L.mamba_block_fwd.argtypes = [vp, vp, fp, fp, vp, vp, fp, fp, fp, vp, vp, bp, vp,
+                                          ctypes.c_size_t, vp]
+            L.mamba_block_fwd.restype = ctypes.c_int
+            L.mamba_block_workspace_bytes.argtypes = [bp]
+            L.mamba_block_workspace_bytes.restype = ctypes.c_size_t
             L.mamba_status_string.argtypes = [ctypes.c_int]
             L.mamba_status_string.restype = ctypes.c_char_p
             L.mamba_abi_version.argtypes = []
@@ -364,5 +378,61 @@ def mamba_gemm_bf16(A, B, b_kcontig=True, c_trans=False, out=None):
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     st = lib().mamba_gemm_bf16(_ptr(A), _ptr(B), _ptr(out), M, N, K, batch, K, ldb, N * K,
                                ldc, M * N, int(bool(b_kcontig)), int(bool(c_trans)), stream)
+    _raise(st)
+    return out
+
+
+def block_dims(hidden, w_in, w_x, w_dt, conv_weight, dstate=DSTATE) -> mamba_block_dims:
+    batch, L, d_model = hidden.shape
+    E = w_in.shape[0] // 2
+    R = w_dt.shape[1]
+    return mamba_block_dims(int(batch), int(L), int(d_model), int(E), int(dstate), int(R),
+                            int(conv_weight.shape[1]), 0)
+
+
+def mamba_block_workspace_bytes(dims: mamba_block_dims) -> int:
+    return int(lib().mamba_block_workspace_bytes(ctypes.byref(dims)))
+
+
+def mamba_block_fwd(hidden, w_in, conv_weight, conv_bias, w_x, w_dt, dt_bias, A, D, w_out,
+                    out=None, workspace=None):
+    """A Mamba block forward (mamba_block_fwd in include/mamba_scan.h).
+
+    hidden: (batch, L, d_model) bf16; w_in (2E, d_model), w_x (R + 32, E), w_dt (E, R),
+    w_out (d_model, E) bf16; conv_weight (E, W), conv_bias (E,), dt_bias (E,), A (E, 16), D (E,)
+    float32 (conv_bias, dt_bias, D may be None).  Returns out (batch, L, d_model) bf16.
+    """
+    if hidden.dim() != 3:
+        raise ValueError("hidden must be (batch, seqlen, d_model)")
+    batch, L, d_model = hidden.shape
+    dev = hidden.device
+    E = w_in.shape[0] // 2
+    R = w_dt.shape[1] if w_dt.dim() == 2 else -1
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(hidden, "hidden", (batch, L, d_model), bf, dev)
+    _check(w_in, "w_in", (2 * E, d_model), bf, dev)
+    _check(w_x, "w_x", (R + 2 * DSTATE, E), bf, dev)
+    _check(w_dt, "w_dt", (E, R), bf, dev)
+    _check(w_out, "w_out", (d_model, E), bf, dev)
+    if conv_weight is None or conv_weight.dim() != 2:
+        raise ValueError("conv_weight must be (d_inner, width)")
+    _check(conv_weight, "conv_weight", (E, conv_weight.shape[1]), f32, dev)
+    _check(conv_bias, "conv_bias", (E,), f32, dev)
+    _check(dt_bias, "dt_bias", (E,), f32, dev)
+    _check(A, "A", (E, DSTATE), f32, dev)
+    _check(D, "D", (E,), f32, dev)
+    if out is None:
+        out = torch.empty((batch, L, d_model), dtype=bf, device=dev)
+    _check(out, "out", (batch, L, d_model), bf, dev)
+    dm = block_dims(hidden, w_in, w_x, w_dt, conv_weight)
+    L_ = lib()
+    ws_bytes = int(L_.mamba_block_workspace_bytes(ctypes.byref(dm)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = L_.mamba_block_fwd(_ptr(hidden), _ptr(w_in), _ptr(conv_weight), _ptr(conv_bias),
+                            _ptr(w_x), _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(w_out),
+                            _ptr(out), ctypes.byref(dm), _ptr(workspace), ws_len, stream)
     _raise(st)
     return out

@@ -29,6 +29,7 @@ BLOCK_ROWS = 64
 _T_BIAS, _T_U, _T_DELTA, _T_Z, _T_B, _T_C, _T_STATE = 0, 1, 2, 3, 4, 5, 6
 _T_DOUT, _T_DLAST = 8, 9  # (7 is the selective-copying stream)
 _T_CONV = 10
+_T_BLOCK = 11
 
 
 @dataclass(frozen=True)
@@ -216,3 +217,46 @@ def selective_copy_values(gap: int, n_seq: int = 400, seed: int = 4705):
     by `gap` distractors, all N(0, 1) fp32; returns an (n_seq, 1 + gap) array (column 0 is the
     target).  One generator per gap: SeedSequence([seed, 7, gap])."""
     return _rng(seed, 7, gap).standard_normal((n_seq, 1 + gap), dtype=np.float32)
+
+
+@dataclass(frozen=True)
+class BlockWorkload:
+    """A Mamba block forward: hidden (batch, seqlen, d_model) -> out (batch, seqlen, d_model)."""
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    d_inner: int
+    dt_rank: int
+    conv_width: int
+    seed: int
+    dstate: int = 16
+
+
+BLOCK_WORKLOADS = {
+    # Mamba-2.8B layer sizes: d_model 2560, expand 2 (d_inner 5120), dt_rank ceil(2560/16) = 160
+    "block_2p8b": BlockWorkload("block_2p8b", 8, 2048, 2560, 5120, 160, 4, 4706),
+}
+
+
+def block_inputs(w: BlockWorkload, seqlen=None):
+    """Seeded hidden states and random weights of a block, all fp32 arrays holding the stored
+    values: hidden and the four projection matrices rounded to bf16; conv taps/bias, dt_bias, A,
+    D in fp32.  Projection weights ~ N(0, 1/fan_in); conv taps and bias as conv_params; dt_bias,
+    A and D as params() with the workloads' bias range [1e-3, 1e-1].  seqlen: optional shorter
+    prefix of the same hidden states (the draws of the first tokens do not depend on it)."""
+    E, R, N, Dm = w.d_inner, w.dt_rank, w.dstate, w.d_model
+    L = w.seqlen if seqlen is None else seqlen
+    r = _rng(w.seed, _T_BLOCK, 0)
+    w_in = round_to_bf16((r.standard_normal((2 * E, Dm)) / np.sqrt(Dm)).astype(np.float32))
+    w_x = round_to_bf16((r.standard_normal((R + 2 * N, E)) / np.sqrt(E)).astype(np.float32))
+    w_dt = round_to_bf16((r.standard_normal((E, R)) / np.sqrt(R)).astype(np.float32))
+    w_out = round_to_bf16((r.standard_normal((Dm, E)) / np.sqrt(E)).astype(np.float32))
+    sw = Workload(w.name, w.batch, E, N, L, "bf16", 1e-3, 1e-1, w.seed)
+    A, D, bias = params(sw)
+    conv_w, conv_b = conv_params(sw, w.conv_width)
+    # hidden: one block of rows per (sequence, token) row of d_model values
+    hid = _normal_rows(w.seed, _T_BLOCK + 1, w.batch * w.seqlen, Dm, None, True)
+    hid = hid.reshape(w.batch, w.seqlen, Dm)[:, :L]
+    return dict(hidden=np.ascontiguousarray(hid), w_in=w_in, conv_w=conv_w, conv_b=conv_b,
+                w_x=w_x, w_dt=w_dt, dt_bias=bias, A=A, D=D, w_out=w_out)
