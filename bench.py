@@ -303,6 +303,52 @@ def bench_conv(w, torch, binding, synth, dev, reps, warm, plain_us):
                 reps=reps, warmup=warm)
 
 
+BF16_MFMA_PEAK = 2.5e15  # dense bf16 MFMA flop/s of the chip
+
+
+def bench_block(torch, binding, synth, dev, reps, warm):
+    """HIP-event time of whole mamba_block_fwd calls at the Mamba-2.8B layer sizes (random
+    weights, seeded hidden states); flops are the four projections' 2*M*N*K."""
+    w = synth.BLOCK_WORKLOADS["block_2p8b"]
+    p = synth.block_inputs(w)
+    bf = ("hidden", "w_in", "w_x", "w_dt", "w_out")
+    t = {k: torch.from_numpy(v).to(dev) for k, v in p.items()}
+    t = {k: (v.to(torch.bfloat16) if k in bf else v) for k, v in t.items()}
+    out = torch.empty_like(t["hidden"])
+    dm = binding.block_dims(t["hidden"], t["w_in"], t["w_x"], t["w_dt"], t["conv_w"])
+    ws = torch.empty(binding.mamba_block_workspace_bytes(dm), dtype=torch.uint8, device=dev)
+
+    def call():
+        binding.mamba_block_fwd(t["hidden"], t["w_in"], t["conv_w"], t["conv_b"], t["w_x"],
+                                t["w_dt"], t["dt_bias"], t["A"], t["D"], t["w_out"], out=out,
+                                workspace=ws)
+    for _ in range(warm):
+        call()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    E, R, Dm, L, B = w.d_inner, w.dt_rank, w.d_model, w.seqlen, w.batch
+    flops = 2.0 * B * L * (2 * E * Dm + (R + 2 * w.dstate) * E + E * R + Dm * E)
+    ok = bool(torch.isfinite(out.float()).all().item())
+    del t, out, ws
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, batch=B, seqlen=L, d_model=Dm, d_inner=E, dt_rank=R,
+                conv_width=w.conv_width, us=med * 1e3, us_p10=ms[len(ms) // 10] * 1e3,
+                us_p90=ms[(len(ms) * 9) // 10] * 1e3, tokens_per_s=B * L / (med * 1e-3),
+                projection_flops=flops, projection_tflops_over_block=flops / (med * 1e-3) / 1e12,
+                mfma_frac_over_block=flops / (med * 1e-3) / BF16_MFMA_PEAK, outputs_finite=ok,
+                reps=reps, warmup=warm,
+                note="whole block (4 GEMMs, conv, scan); per-kernel split in profiles/")
+
+
 def other_workloads(torch, binding, synth, dev):
     """Every other whole-sequence workload, and the sequence-length sweep (batch 1, 1536
     channels, fp32) for the linear-in-L claim."""
@@ -350,6 +396,9 @@ def main():
     ap.add_argument("--step-steps", type=int, default=1000)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-conv", action="store_true", help="skip the fused-conv forward timing")
+    ap.add_argument("--no-block", action="store_true", help="skip the Mamba block timing")
+    ap.add_argument("--block-only", action="store_true",
+                    help="time only the Mamba block forward (for profiling runs)")
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--bwd-warmup", type=int, default=60)
     ap.add_argument("--bwd-only", action="store_true",
@@ -382,6 +431,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.block_only:
+        print(json.dumps(bench_block(torch, binding, synth, dev, 10, 5)), flush=True)
+        return 0
     if args.bwd_only:
         print(json.dumps(bench_backward(w, torch, binding, dev, args.bwd_steps,
                                         args.bwd_warmup)), flush=True)
@@ -479,6 +531,8 @@ def main():
                                                kern_ms[len(kern_ms) // 2] * 1e3)
     if not args.no_bwd:
         rec["backward"] = bench_backward(w, torch, binding, dev, args.bwd_steps, args.bwd_warmup)
+    if not args.no_block:
+        rec["block_forward"] = bench_block(torch, binding, synth, dev, 10, 5)
     if not args.no_step:
         del t, out
         torch.cuda.empty_cache()

@@ -1,13 +1,14 @@
 // mamba_gemm.hip -- bf16 MFMA GEMM for gfx950 (see mamba_gemm.h).
 //
 // Workgroup tile 128 x 128 (M x N), K step 64, 256 threads = 4 waves in a 2 x 2 grid, each wave
-// 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 64 registers).
+// 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 64 registers); the tile
+// shape is a template (TileShape) so that other shapes can be measured.
 // Operand layouts of that instruction on gfx950 (checked with an in-bounds probe): lane l holds
 // A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; accumulator element i of lane l is
 // C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
-// Both operand tiles live in LDS with K contiguous (rows of 64 bf16 padded to 72: 144-byte row
-// pitch, so the 16-byte fragment reads of 32 consecutive rows spread over all banks), double
-// buffered: the next K step is loaded into registers while the current one is multiplied.
+// Both operand tiles live in LDS with K contiguous, rows padded by 16 bytes (pitch 144 bytes: the
+// 16-byte fragment reads of 8 consecutive rows hit all 32 banks), double buffered:
+// the next K step is loaded into registers while the current one is multiplied.
 // An N-contiguous B tile is transposed in registers on its way to LDS (4 k-rows x 8 columns per
 // thread, packed into 8-byte column pieces).
 #include "mamba_gemm.h"
@@ -17,14 +18,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int kGM = 128, kGN = 128, kGK = 64;
-constexpr int kRow = kGK + 8;  // bf16 per LDS row
-
-struct __align__(16) GemmSmem {
-  uint16_t a[2][kGM * kRow];
-  uint16_t b[2][kGN * kRow];
-};
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p, bool ok) {
   return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
@@ -38,34 +31,59 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <bool kBK>
+// Tile shape: 4 waves in a 2 x 2 grid, each wave kWM x kWN MFMA tiles of 32 x 32, so the
+// workgroup tile is (64 kWM) x (64 kWN); K advances kBK per step.  Every thread stages 2 or 4
+// 16-byte words of A and 4 of B per step.
+template <int kWM, int kWN, int kBK>
+struct TileShape {
+  static constexpr int TM = 64 * kWM, TN = 64 * kWN;
+  static constexpr int Row = kBK + 8;                 // bf16 per LDS row (pitch 16 B beyond K)
+  static constexpr int WPR = kBK / 8;                 // 16-byte words per K-contiguous row
+  static constexpr int PA = TM * WPR / 256;           // words per thread, A
+  static constexpr int PB = TN * WPR / 256;           // words per thread, K-contiguous B
+  static constexpr int TPRA = WPR / PA, TPRB = WPR / PB;
+  static_assert((PA == 2 || PA == 4) && PB == 4, "staging assumes 2 or 4 words of A, 4 of B");
+  static_assert((kBK / 4) * (TN / 8) == 256, "N-contiguous staging covers the tile");
+};
+
+template <int kWM, int kWN, int kBK>
+struct __align__(16) GemmSmem {
+  using S = TileShape<kWM, kWN, kBK>;
+  uint16_t a[2][S::TM * S::Row];
+  uint16_t b[2][S::TN * S::Row];
+};
+
+template <int kWM, int kWN, int kBK, bool kBKc>
 struct GemmThread {
+  using S = TileShape<kWM, kWN, kBK>;
   const GemmArgs& p;
-  GemmSmem& sm;
-  int tid, lane, wm, wn;
-  int64_t m0, n0, bidx;
+  GemmSmem<kWM, kWN, kBK>& sm;
+  int tid;
+  int64_t m0, n0;
   const uint16_t* Bb;
-  uint4 ra[4], rb[4];
+  uint4 ra[S::PA], rb[4];
 
-  __device__ GemmThread(const GemmArgs& args, GemmSmem& s) : p(args), sm(s) {}
+  __device__ GemmThread(const GemmArgs& args, GemmSmem<kWM, kWN, kBK>& s) : p(args), sm(s) {}
 
-  // global -> registers for the K step starting at k0
+  // global -> registers for the K step starting at k0 (zero outside the matrices)
   __device__ __forceinline__ void load(int64_t k0) {
-    {  // A: thread -> row tid/2, 32 consecutive k
-      const int r = tid >> 1, kh = (tid & 1) * 32;
+    {
+      const int r = tid / S::TPRA, kw = (tid % S::TPRA) * S::PA * 8;
       const int64_t m = m0 + r;
-      const uint16_t* src = p.A + m * p.lda + k0 + kh;
+      const uint16_t* src = p.A + m * p.lda + k0 + kw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ra[j] = ld16(src + 8 * j, m < p.M && k0 + kh + 8 * j < p.K);
+      for (int j = 0; j < S::PA; ++j)
+        ra[j] = ld16(src + 8 * j, m < p.M && k0 + kw + 8 * j < p.K);
     }
-    if (kBK) {  // B K-contiguous: as A, rows are columns n
-      const int r = tid >> 1, kh = (tid & 1) * 32;
+    if (kBKc) {
+      const int r = tid / S::TPRB, kw = (tid % S::TPRB) * 4 * 8;
       const int64_t n = n0 + r;
-      const uint16_t* src = Bb + n * p.ldb + k0 + kh;
+      const uint16_t* src = Bb + n * p.ldb + k0 + kw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rb[j] = ld16(src + 8 * j, n < p.N && k0 + kh + 8 * j < p.K);
-    } else {    // B N-contiguous: thread -> k rows 4*(tid/16) .. +3, columns 8*(tid%16) .. +7
-      const int kg = tid >> 4, ng = tid & 15;
+      for (int j = 0; j < 4; ++j) rb[j] = ld16(src + 8 * j, n < p.N && k0 + kw + 8 * j < p.K);
+    } else {  // thread -> k rows 4 kg .. 4 kg + 3, columns 8 ng .. 8 ng + 7
+      constexpr int NG = S::TN / 8;
+      const int kg = tid / NG, ng = tid % NG;
       const int64_t n = n0 + 8 * ng;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -78,79 +96,80 @@ struct GemmThread {
   // registers -> LDS buffer `buf` (K contiguous rows)
   __device__ __forceinline__ void store(int buf) {
     {
-      const int r = tid >> 1, kh = (tid & 1) * 32;
-      uint4* dst = reinterpret_cast<uint4*>(&sm.a[buf][r * kRow + kh]);
+      const int r = tid / S::TPRA, kw = (tid % S::TPRA) * S::PA * 8;
+      uint4* dst = reinterpret_cast<uint4*>(&sm.a[buf][r * S::Row + kw]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = ra[j];
+      for (int j = 0; j < S::PA; ++j) dst[j] = ra[j];
     }
-    if (kBK) {
-      const int r = tid >> 1, kh = (tid & 1) * 32;
-      uint4* dst = reinterpret_cast<uint4*>(&sm.b[buf][r * kRow + kh]);
+    if (kBKc) {
+      const int r = tid / S::TPRB, kw = (tid % S::TPRB) * 4 * 8;
+      uint4* dst = reinterpret_cast<uint4*>(&sm.b[buf][r * S::Row + kw]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j] = rb[j];
     } else {
-      const int kg = tid >> 4, ng = tid & 15;
+      constexpr int NG = S::TN / 8;
+      const int kg = tid / NG, ng = tid % NG;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        // column 8*ng + c: k rows 4kg .. 4kg+3 -> one 8-byte piece
+        // column 8 ng + c: k rows 4 kg .. 4 kg + 3 -> one 8-byte piece
         const int wi = c >> 1, h = c & 1;
         const uint32_t lo = pick(word(rb[0], wi), word(rb[1], wi), h);
         const uint32_t hi = pick(word(rb[2], wi), word(rb[3], wi), h);
-        *reinterpret_cast<uint2*>(&sm.b[buf][(8 * ng + c) * kRow + 4 * kg]) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(&sm.b[buf][(8 * ng + c) * S::Row + 4 * kg]) =
+            make_uint2(lo, hi);
       }
     }
   }
 };
 
-template <bool kBK>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
-  __shared__ GemmSmem sm;
-  GemmThread<kBK> th(p, sm);
+template <int kWM, int kWN, int kBK, bool kBKc>
+__global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(GemmArgs p) {
+  using S = TileShape<kWM, kWN, kBK>;
+  __shared__ GemmSmem<kWM, kWN, kBK> sm;
+  GemmThread<kWM, kWN, kBK, kBKc> th(p, sm);
   th.tid = threadIdx.x;
-  th.lane = th.tid & 63;
+  const int lane = th.tid & 63;
   const int w = th.tid >> 6;
-  th.wm = w >> 1;
-  th.wn = w & 1;
+  const int wm = w >> 1, wn = w & 1;
   const int64_t mt = blockIdx.x / p.ntiles;
   const int64_t nt = blockIdx.x - mt * p.ntiles;
-  th.m0 = mt * kGM;
-  th.n0 = nt * kGN;
-  th.bidx = blockIdx.y;
-  th.Bb = p.B + th.bidx * p.b_bstride;
-  const int lane = th.lane;
+  th.m0 = mt * S::TM;
+  th.n0 = nt * S::TN;
+  const int64_t bidx = blockIdx.y;
+  th.Bb = p.B + bidx * p.b_bstride;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[kWM][kWN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kWM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kWN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int64_t nk = (p.K + kGK - 1) / kGK;
+  const int64_t nk = (p.K + kBK - 1) / kBK;
   th.load(0);
   th.store(0);
   __syncthreads();
   for (int64_t ks = 0; ks < nk; ++ks) {
     const int buf = (int)(ks & 1);
-    if (ks + 1 < nk) th.load((ks + 1) * kGK);
+    if (ks + 1 < nk) th.load((ks + 1) * kBK);
     const uint16_t* As = sm.a[buf];
     const uint16_t* Bs = sm.b[buf];
 #pragma unroll
-    for (int kk = 0; kk < kGK / 16; ++kk) {
-      bf16x8_t fa[2], fb[2];
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8_t fa[kWM], fb[kWN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kWM; ++i)
         fa[i] = *reinterpret_cast<const bf16x8_t*>(
-            &As[(64 * th.wm + 32 * i + (lane & 31)) * kRow + 16 * kk + 8 * (lane >> 5)]);
+            &As[(S::TM / 2 * wm + 32 * i + (lane & 31)) * S::Row + 16 * kk + 8 * (lane >> 5)]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kWN; ++j)
         fb[j] = *reinterpret_cast<const bf16x8_t*>(
-            &Bs[(64 * th.wn + 32 * j + (lane & 31)) * kRow + 16 * kk + 8 * (lane >> 5)]);
+            &Bs[(S::TN / 2 * wn + 32 * j + (lane & 31)) * S::Row + 16 * kk + 8 * (lane >> 5)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kWM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kWN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     if (ks + 1 < nk) {
@@ -161,14 +180,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
 
   // ---- epilogue: route rows to their destination, round to bf16
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kWM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = th.n0 + 64 * th.wn + 32 * j + (lane & 31);
+    for (int j = 0; j < kWN; ++j) {
+      const int64_t n = th.n0 + S::TN / 2 * wn + 32 * j + (lane & 31);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // rows mq .. mq+3 of this lane (4 consecutive rows, inside one destination)
-        const int64_t mq = th.m0 + 64 * th.wm + 32 * i + 8 * q + 4 * (lane >> 5);
+        const int64_t mq = th.m0 + S::TM / 2 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
         if (mq >= p.M || n >= p.N) continue;
         int di = 0;
         while (di + 1 < p.ndst && mq >= p.dst[di].m1) ++di;
@@ -176,10 +195,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
         if (d.ptr == nullptr || mq < d.m0 || mq >= d.m1) continue;
         const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
         const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        uint16_t* base = d.ptr + th.bidx * d.bstride;
+        uint16_t* base = d.ptr + bidx * d.bstride;
         const int64_t r = mq - d.m0;
         if (d.trans) {
-          const uint2 w2 = make_uint2(pack_bf16(make_float2(v0, v1)), pack_bf16(make_float2(v2, v3)));
+          const uint2 w2 =
+              make_uint2(pack_bf16(make_float2(v0, v1)), pack_bf16(make_float2(v2, v3)));
           *reinterpret_cast<uint2*>(base + n * d.ld + r) = w2;
         } else {
           const uint32_t w01 = pack_bf16(make_float2(v0, v1));
@@ -192,6 +212,22 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs p) {
       }
     }
   }
+}
+
+template <int kWM, int kWN, int kBK>
+int launch_shape(const GemmArgs& a0, bool b_kcontig, int64_t batch, hipStream_t s) {
+  using S = TileShape<kWM, kWN, kBK>;
+  GemmArgs a = a0;
+  a.mtiles = (int32_t)((a.M + S::TM - 1) / S::TM);
+  a.ntiles = (int32_t)((a.N + S::TN - 1) / S::TN);
+  if ((int64_t)a.mtiles * a.ntiles > 0x7fffffffLL || batch > 65535 || batch < 1)
+    return MAMBA_ERR_SHAPE;
+  const dim3 grid((unsigned)(a.mtiles * a.ntiles), (unsigned)batch);
+  if (b_kcontig)
+    hipLaunchKernelGGL((gemm_kernel<kWM, kWN, kBK, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<kWM, kWN, kBK, false>), grid, dim3(256), 0, s, a);
+  return launch_status();
 }
 
 }  // namespace
@@ -213,18 +249,12 @@ int gemm_check(const GemmArgs& a) {
   return MAMBA_OK;
 }
 
-int launch_gemm(const GemmArgs& a0, bool b_kcontig, int64_t batch, hipStream_t s) {
-  GemmArgs a = a0;
-  a.mtiles = (int32_t)((a.M + kGM - 1) / kGM);
-  a.ntiles = (int32_t)((a.N + kGN - 1) / kGN);
-  if ((int64_t)a.mtiles * a.ntiles > 0x7fffffffLL || batch > 65535 || batch < 1)
-    return MAMBA_ERR_SHAPE;
-  const dim3 grid((unsigned)(a.mtiles * a.ntiles), (unsigned)batch);
-  if (b_kcontig)
-    hipLaunchKernelGGL((gemm_kernel<true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<false>), grid, dim3(256), 0, s, a);
-  return launch_status();
+int launch_gemm(const GemmArgs& a, bool b_kcontig, int64_t batch, hipStream_t s) {
+  // 128 x 128 x 64 tiles, two workgroups per CU.  Measured at the Mamba-2.8B projection shapes,
+  // 256 x 256 x 32 (one workgroup per CU, 4 x 4 tiles per wave in AGPRs) and 128 x 256 x 32 were
+  // 10-25% slower: with register staging the per-step wait for the next tile's loads, its LDS
+  // store and the barrier dominate, and shallower K steps pay them more often.
+  return launch_shape<2, 2, 64>(a, b_kcontig, batch, s);
 }
 
 }  // namespace mamba

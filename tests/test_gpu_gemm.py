@@ -34,8 +34,10 @@ def bf16(rng, shape, scale=1.0):
     return synth.round_to_bf16((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
+# the last two are many-tile shapes, the second with ragged M, N and K tails
 SHAPES = [(16, 8, 8, 1), (128, 128, 64, 1), (144, 200, 136, 2), (256, 384, 520, 3),
-          (192, 264, 5120, 2), (5120, 136, 160, 1), (48, 1000, 72, 2)]
+          (192, 264, 5120, 2), (5120, 136, 160, 1), (48, 1000, 72, 2),
+          (4096, 2048, 512, 4), (4112, 2056, 520, 4)]
 
 
 @pytest.mark.parametrize("b_kcontig", [True, False])
@@ -56,7 +58,7 @@ def test_gemm_matches_fp64(shape, b_kcontig, c_trans):
     C = C.float().cpu().numpy()
     if c_trans:
         C = C.transpose(0, 2, 1)
-    ref = np.einsum("mk,bkn->bmn", A.astype(np.float64), Bm.astype(np.float64))
+    ref = np.matmul(A.astype(np.float64)[None], Bm.astype(np.float64))
     e = rel_err(C, ref)
     print(f"[gemm] rel err {e:.2e}", flush=True)
     assert e <= 1e-2
