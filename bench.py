@@ -14,7 +14,6 @@ is reported next to it.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -48,10 +47,14 @@ BWD_OPS_PER_CHANNEL_STEP = 272 + 37
 CONV_OPS_PER_CHANNEL_STEP = ALU_OPS_PER_CHANNEL_STEP + 4 + 7
 
 
-def kernel_source_hash() -> str:
+# Sources of the forward scan and state-update kernels (the counters in profiles/ are tied to them)
+FWD_KERNEL_SOURCES = ("mamba_common.h", "mamba_scan.hip")
+
+
+def kernel_source_hash(files=FWD_KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_47_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in files:
+        with open(os.path.join(ROOT, "selective_state_space_47_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

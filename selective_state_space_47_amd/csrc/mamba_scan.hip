@@ -39,7 +39,9 @@ struct __align__(16) ScanSmem {
   float y[kWaves][kChW * 8][kYStride];   // partial readouts per lane and token (first: short
                                          // immediate offsets)
   float4 bc[kTT][8];                     // (B_2g, B_2g+1, C_2g, C_2g+1) per token and lane group
-  float2 dd[kWaves][kTS][kChW];          // (Delta, Delta*u) per token and channel
+  float2 dd[kWaves][kTS][kChW + 1];      // (Delta, Delta*u) per token and channel; the padded
+                                         // row (18 floats) makes the writes of the 8 lanes of a
+                                         // channel (tokens 2g, 2g+1) hit distinct banks
 };
 
 // Per-thread state of one workgroup: 32 channels of one sequence over one chunk of tokens.
@@ -64,17 +66,18 @@ struct ScanThread {
   const Tin* __restrict__ Z;
   Tin* __restrict__ O;
   float* __restrict__ CK;  // checkpoint row of this lane's channel, offset by 2g
-  const Tin* __restrict__ BCrow;
-  int w, lane, c, g, sq, sslot, sg;
+  const Tin* __restrict__ BC0;  // B row 2*bg of the sequence (row 2*bg+1 follows at +L)
+  const Tin* __restrict__ CC0;  // C row 2*bg
+  int w, lane, c, g, btp, bg;
   bool dvalid;
-  int64_t row, t_end;
+  int64_t row, t_end, row_stride_L;
   float a0, a1, bias, dskip;
   float h0 = 0.f, h1 = 0.f, dsum = 0.f;
   float cw0, cw1, cw2, cw3, cbias;  // conv taps, oldest first, and bias (kConv)
   float px0 = 0.f, px1 = 0.f;       // x of this lane's token pair in the previous sub-tile
   Tin* __restrict__ UO;             // optional store of u (kConv, main pass)
   Raw ru[kSub], rd[kSub], rz[kSub];
-  Raw8<Tin> rbc;
+  Raw rbc[4];  // B_2bg, B_2bg+1, C_2bg, C_2bg+1 at the staging thread's token pair
 
   __device__ __forceinline__ ScanThread(ScanSmem& s) : sm(s) {}
 
@@ -93,8 +96,16 @@ struct ScanThread {
     rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
     if (kGate) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
   }
+  // B/C staging loads: thread -> token pair btp (0..31) of the tile, lane group bg (0..7); it
+  // loads the pairs of rows 2bg, 2bg+1 of B and of C and later writes the two float4s of its
+  // tokens, so every LDS write is a conflict-free 16-byte row piece
   __device__ __forceinline__ void load_bc(int64_t t0) {
-    rbc = load8<kVec>(BCrow, t0 + 8 * sq, t0 + 8 * sq, t_end);
+    const int64_t t = t0 + 2 * btp;
+    const bool ok0 = t < t_end, ok1 = t + 1 < t_end;
+    rbc[0] = load_pair<kVec>(BC0, t, ok0, ok1);
+    rbc[1] = load_pair<kVec>(BC0 + row_stride_L, t, ok0, ok1);
+    rbc[2] = load_pair<kVec>(CC0, t, ok0, ok1);
+    rbc[3] = load_pair<kVec>(CC0 + row_stride_L, t, ok0, ok1);
   }
   // prefetch of sub-tile s of the tile starting at tn (uniform branch)
   __device__ __forceinline__ void prefetch_sub(int64_t tn, int s) {
@@ -127,9 +138,12 @@ struct ScanThread {
   __device__ __forceinline__ void tile(int64_t t0) {
     const int64_t tn = t0 + kTT;
     __syncthreads();  // every wave is done reading the previous tile's B/C
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      reinterpret_cast<float*>(&sm.bc[8 * sq + i][sg])[sslot] = elem8(rbc, i);
+    {
+      const float2 b0 = unpack(rbc[0]), b1 = unpack(rbc[1]);
+      const float2 c0 = unpack(rbc[2]), c1 = unpack(rbc[3]);
+      sm.bc[2 * btp][bg] = make_float4(b0.x, b1.x, c0.x, c1.x);
+      sm.bc[2 * btp + 1][bg] = make_float4(b0.y, b1.y, c0.y, c1.y);
+    }
     if (tn < t_end) load_bc(tn);
     __syncthreads();
 
@@ -288,13 +302,12 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
     th.h1 = h1;
   }
 
-  // B/C staging assignment: thread -> (row r of the 32 B/C rows, 8-token segment q)
-  const int sr = tid >> 3;
-  th.sq = tid & 7;
-  const int sn = sr & 15;
-  th.BCrow = (sr < 16 ? Bm : Cm) + (b * kN + sn) * p.L;
-  th.sslot = (sr < 16 ? 0 : 2) + (sn & 1);
-  th.sg = sn >> 1;
+  // B/C staging assignment: thread -> (token pair 8w + lane/8 of the tile, lane group lane%8)
+  th.btp = 8 * th.w + (th.lane >> 3);
+  th.bg = th.lane & 7;
+  th.row_stride_L = p.L;
+  th.BC0 = Bm + (b * kN + 2 * th.bg) * p.L;
+  th.CC0 = Cm + (b * kN + 2 * th.bg) * p.L;
 
   // raw registers are prefetched one tile ahead: sub-tile s of the next tile is loaded as soon
   // as sub-tile s of the current tile has consumed its registers, B/C right after staging
