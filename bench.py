@@ -90,8 +90,10 @@ def parse_counters(fetch_csv, write_csv, out_json, scan_bytes_alg):
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         per = read(path, counter)
         scan = [v for k, vs in per.items() if "scan_kernel" in k for v in vs]
-        other = [(max(vs), k) for k, vs in per.items() if "scan_kernel" not in k]
-        copy = per[max(other)[1]] if other else []
+        # the calibration copy: torch.mul(a, 1.0, out=b) over 1 GiB (--calib-copy); its largest
+        # dispatches (smaller ones of the same kernel come from torch's own setup)
+        copy_k = [k for k in per if "MulFunctor<float>" in k and "AUnaryFunctor" in k]
+        copy = sorted(per[copy_k[0]])[-3:] if copy_k else []
         if not scan or not copy:
             raise SystemExit(f"{counter}: scan or copy kernel not found in {path}: {list(per)}")
         scan_kib = sorted(scan)[len(scan) // 2]
