@@ -67,7 +67,9 @@ struct BwdArgs {
 
 struct __align__(16) BwdSmem {
   float4 bc[kBT][8];                  // (B_2g, B_2g+1, C_2g, C_2g+1) per token and lane group
-  float4 dd[kWaves][kBT][kChW];       // (Delta, Delta*u, dy, -) per token and channel
+  float4 dd[kWaves][kBT][kChW + 1];   // (Delta, Delta*u, dy, -) per token and channel; the
+                                      // padded row (36 floats) spreads the 16-byte writes of a
+                                      // channel's 8 lanes (tokens 0..7) over all banks
   float red[kWaves][kBT][32];         // per-wave channel sums of (dB, dC) per token
   union Scratch {                     // per-wave exchange buffer, used in turn for:
     float y[kChW * 8][kSYs];          //   partial readouts of the block's tokens
@@ -132,12 +134,13 @@ __global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
     if (!dvalid) car0 = car1 = 0.f;
   }
 
-  // B/C staging: thread -> (row sr of the 32 B/C rows, token sq of the block)
-  const int sr = tid >> 3, sq = tid & 7, sn = sr & 15;
-  // waves 0-1 stage B rows, waves 2-3 C rows: the row base is wave-uniform (scalar registers)
-  const Tin* __restrict__ BCm = __builtin_amdgcn_readfirstlane(w) < 2 ? Bm : Cm;
+  // B/C staging: thread -> (row sr of the 32 B/C rows: B 0..15, C 16..31; token sq of the
+  // block).  Consecutive lanes take consecutive rows, so the 32 lanes of a write pass hit 32
+  // different banks (row n goes to float n of its lane group's float4).
+  const int sr = tid & 31, sq = tid >> 5, sn = sr & 15;
+  const bool srB = sr < 16;
   const int64_t bcrow = (b * kN + sn) * p.L;
-  const int sslot = (sr < 16 ? 0 : 2) + (sn & 1), sgrp = sn >> 1;
+  const int sslot = (srB ? 0 : 2) + (sn & 1), sgrp = sn >> 1;
 
   float* __restrict__ PBC = p.part_bc + (b * p.dblocks + blk) * p.L * 32;
   float dA0 = 0.f, dA1 = 0.f, dDacc = 0.f, dbacc = 0.f, dsum = 0.f;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
     const float xl = ld_f32(U, ix), drl = ld_f32(DL, ix), gol = ld_f32(GO, ix);
     const float zl = kGate ? ld_f32(Z, ix) : 0.f;
     const float2 hs = *reinterpret_cast<const float2*>(p.ckpt + ick);
-    const float bcl = ld_f32(BCm, ibc);
+    const float bcl = srB ? ld_f32(Bm, ibc) : ld_f32(Cm, ibc);
     const float x = ok ? xl : 0.f;
     const float draw = ok ? drl : 0.f;
     const float zv = ok ? zl : 0.f;
