@@ -25,6 +25,7 @@ struct GemmArgs {
   int64_t lda, ldb, b_bstride;
   int64_t M, N, K;
   int32_t mtiles, ntiles, ndst;
+  int64_t batch;
   GemmDest dst[3];
 };
 

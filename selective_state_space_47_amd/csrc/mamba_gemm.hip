@@ -81,9 +81,12 @@ struct GemmThread {
       const uint16_t* src = Bb + n * p.ldb + k0 + kw;
 #pragma unroll
       for (int j = 0; j < 4; ++j) rb[j] = ld16(src + 8 * j, n < p.N && k0 + kw + 8 * j < p.K);
-    } else {  // thread -> k rows 4 kg .. 4 kg + 3, columns 8 ng .. 8 ng + 7
-      constexpr int NG = S::TN / 8;
-      const int kg = tid / NG, ng = tid % NG;
+    } else {  // thread -> k rows 4 kg .. 4 kg + 3, columns 8 ng .. 8 ng + 7; consecutive lanes
+              // take consecutive k groups, so the 8-byte column pieces they write land in
+              // different banks (lanes of equal kg would all hit one bank: 8 rows of 144 bytes
+              // are a multiple of the 128-byte bank cycle)
+      constexpr int KG = kBK / 4;
+      const int kg = tid % KG, ng = tid / KG;
       const int64_t n = n0 + 8 * ng;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -107,8 +110,8 @@ struct GemmThread {
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j] = rb[j];
     } else {
-      constexpr int NG = S::TN / 8;
-      const int kg = tid / NG, ng = tid % NG;
+      constexpr int KG = kBK / 4;
+      const int kg = tid % KG, ng = tid / KG;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         // column 8 ng + c: k rows 4 kg .. 4 kg + 3 -> one 8-byte piece
@@ -122,6 +125,29 @@ struct GemmThread {
   }
 };
 
+// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2), so
+// workgroup w runs on XCD w % 8.  Each XCD is given a contiguous range of the tile sequence, and
+// the sequence walks groups of kGroupM row tiles column by column: consecutive tiles on one XCD
+// share A rows (weights) and B columns (activations) while they are in its L2.
+constexpr int64_t kXcds = 8;
+constexpr int64_t kGroupM = 4;
+
+__device__ __forceinline__ void tile_of(const GemmArgs& p, int64_t w, int64_t* b, int64_t* mt,
+                                        int64_t* nt) {
+  const int64_t per_b = (int64_t)p.mtiles * p.ntiles;
+  const int64_t total = per_b * p.batch;
+  const int64_t x = w % kXcds, idx = w / kXcds;
+  const int64_t q = total / kXcds, r = total % kXcds;
+  const int64_t pos = x * q + (x < r ? x : r) + idx;  // XCD x owns [x q + min(x, r), +count)
+  *b = pos / per_b;
+  const int64_t t = pos - *b * per_b;
+  const int64_t gsize = kGroupM * p.ntiles;
+  const int64_t gi = t / gsize, tg = t - gi * gsize;
+  const int64_t gm = min((int64_t)kGroupM, (int64_t)p.mtiles - gi * kGroupM);
+  *mt = gi * kGroupM + tg % gm;
+  *nt = tg / gm;
+}
+
 template <int kWM, int kWN, int kBK, bool kBKc>
 __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(GemmArgs p) {
   using S = TileShape<kWM, kWN, kBK>;
@@ -131,11 +157,10 @@ __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(Ge
   const int lane = th.tid & 63;
   const int w = th.tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int64_t mt = blockIdx.x / p.ntiles;
-  const int64_t nt = blockIdx.x - mt * p.ntiles;
+  int64_t bidx, mt, nt;
+  tile_of(p, blockIdx.x, &bidx, &mt, &nt);
   th.m0 = mt * S::TM;
   th.n0 = nt * S::TN;
-  const int64_t bidx = blockIdx.y;
   th.Bb = p.B + bidx * p.b_bstride;
 
   f32x16_t acc[kWM][kWN];
@@ -220,9 +245,10 @@ int launch_shape(const GemmArgs& a0, bool b_kcontig, int64_t batch, hipStream_t 
   GemmArgs a = a0;
   a.mtiles = (int32_t)((a.M + S::TM - 1) / S::TM);
   a.ntiles = (int32_t)((a.N + S::TN - 1) / S::TN);
-  if ((int64_t)a.mtiles * a.ntiles > 0x7fffffffLL || batch > 65535 || batch < 1)
+  a.batch = batch;
+  if ((int64_t)a.mtiles * a.ntiles * batch > 0x7fffffffLL || batch > 65535 || batch < 1)
     return MAMBA_ERR_SHAPE;
-  const dim3 grid((unsigned)(a.mtiles * a.ntiles), (unsigned)batch);
+  const dim3 grid((unsigned)((int64_t)a.mtiles * a.ntiles * batch));
   if (b_kcontig)
     hipLaunchKernelGGL((gemm_kernel<kWM, kWN, kBK, true>), grid, dim3(256), 0, s, a);
   else
