@@ -361,46 +361,72 @@ struct StepArgs {
   int32_t softplus;
 };
 
-// Four lanes per channel, four states per lane (one float4 of the state row each); 16 channels
-// per wave, 64 per workgroup.  Grid: (channel blocks of 64, batch) -- no integer division.
-// The step is bound by the state read and write.
+// Four lanes per channel, four states per lane (one float4 of the state row each).  Each thread
+// serves kStepCh channels 64 apart, and every load of all of them is issued before any compute:
+// the step is bound by the state read and write, and with one 16-byte state load per thread the
+// memory system holds too few bytes in flight to reach HBM bandwidth.  A workgroup covers
+// 64 * kStepCh consecutive channels of one sequence.  Grid: (channel blocks, batch).
+constexpr int kStepCh = 2;
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
   const int q = threadIdx.x & 3;
-  const int64_t d = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-  if (d >= p.dim) return;
+  const int64_t d0 = (int64_t)blockIdx.x * (64 * kStepCh) + (threadIdx.x >> 2);
   const int64_t b = blockIdx.y;
-  const int64_t ch = b * p.dim + d;
   const Tin* U = static_cast<const Tin*>(p.u);
   const Tin* DL = static_cast<const Tin*>(p.delta);
+  const Tin* Z = static_cast<const Tin*>(p.z);
   const Tin* Bm = static_cast<const Tin*>(p.B);
   const Tin* Cm = static_cast<const Tin*>(p.C);
-
-  float4* sp = reinterpret_cast<float4*>(p.state + ch * kN) + q;
-  float4 h = *sp;
-  const float4 A4 = *(reinterpret_cast<const float4*>(p.A + d * kN) + q);
-  const float x = ld_f32(U, ch);
-  float dl = ld_f32(DL, ch) + (p.bias ? p.bias[d] : 0.f);
-  if (p.softplus) dl = softplus_f32(dl);
-  const float du = dl * x;
   const int64_t bo = b * kN + 4 * q;
-  float y;
-  h.x = fmaf(fast_exp2(dl * A4.x * kLog2e), h.x, du * ld_f32(Bm, bo + 0));
-  h.y = fmaf(fast_exp2(dl * A4.y * kLog2e), h.y, du * ld_f32(Bm, bo + 1));
-  h.z = fmaf(fast_exp2(dl * A4.z * kLog2e), h.z, du * ld_f32(Bm, bo + 2));
-  h.w = fmaf(fast_exp2(dl * A4.w * kLog2e), h.w, du * ld_f32(Bm, bo + 3));
-  y = ld_f32(Cm, bo + 0) * h.x;
-  y = fmaf(ld_f32(Cm, bo + 1), h.y, y);
-  y = fmaf(ld_f32(Cm, bo + 2), h.z, y);
-  y = fmaf(ld_f32(Cm, bo + 3), h.w, y);
-  *sp = h;
-  // sum the four partial readouts of the channel (fixed order)
-  y += __shfl_xor(y, 1);
-  y += __shfl_xor(y, 2);
-  if (q == 0) {
-    if (p.D) y = fmaf(p.D[d], x, y);
-    if (p.z) y *= silu_f32(ld_f32(static_cast<const Tin*>(p.z), ch));
-    st_out(static_cast<Tin*>(p.out), ch, y);
+  float bb[4], cc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bb[i] = ld_f32(Bm, bo + i);
+    cc[i] = ld_f32(Cm, bo + i);
+  }
+  float4 h[kStepCh], A4[kStepCh];
+  float x[kStepCh], dr[kStepCh], zz[kStepCh], bias[kStepCh], dsk[kStepCh];
+  bool ok[kStepCh];
+#pragma unroll
+  for (int j = 0; j < kStepCh; ++j) {
+    const int64_t d = d0 + 64 * j;
+    ok[j] = d < p.dim;
+    const int64_t dc = ok[j] ? d : p.dim - 1;  // loads stay unconditional and in bounds
+    const int64_t ch = b * p.dim + dc;
+    h[j] = *(reinterpret_cast<const float4*>(p.state + ch * kN) + q);
+    A4[j] = *(reinterpret_cast<const float4*>(p.A + dc * kN) + q);
+    x[j] = ld_f32(U, ch);
+    dr[j] = ld_f32(DL, ch);
+    zz[j] = p.z ? ld_f32(Z, ch) : 0.f;
+    bias[j] = p.bias ? p.bias[dc] : 0.f;
+    dsk[j] = p.D ? p.D[dc] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kStepCh; ++j) {
+    const int64_t d = d0 + 64 * j;
+    const int64_t ch = b * p.dim + d;
+    float dl = dr[j] + bias[j];
+    if (p.softplus) dl = softplus_f32(dl);
+    const float du = dl * x[j];
+    float4 hv = h[j];
+    hv.x = fmaf(fast_exp2(dl * A4[j].x * kLog2e), hv.x, du * bb[0]);
+    hv.y = fmaf(fast_exp2(dl * A4[j].y * kLog2e), hv.y, du * bb[1]);
+    hv.z = fmaf(fast_exp2(dl * A4[j].z * kLog2e), hv.z, du * bb[2]);
+    hv.w = fmaf(fast_exp2(dl * A4[j].w * kLog2e), hv.w, du * bb[3]);
+    float y = cc[0] * hv.x;
+    y = fmaf(cc[1], hv.y, y);
+    y = fmaf(cc[2], hv.z, y);
+    y = fmaf(cc[3], hv.w, y);
+    if (ok[j]) *(reinterpret_cast<float4*>(p.state + ch * kN) + q) = hv;
+    // sum the four partial readouts of the channel (fixed order)
+    y += __shfl_xor(y, 1);
+    y += __shfl_xor(y, 2);
+    if (q == 0 && ok[j]) {
+      y = fmaf(dsk[j], x[j], y);
+      if (p.z) y *= silu_f32(zz[j]);
+      st_out(static_cast<Tin*>(p.out), ch, y);
+    }
   }
 }
 
@@ -554,7 +580,7 @@ int mamba_state_update(float* state, const void* u, const void* delta, const flo
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
   a.bias = delta_bias; a.out = out; a.batch = dims->batch; a.dim = dims->dim;
   a.softplus = softplus_flag ? 1 : 0;
-  const int64_t xblocks = (dims->dim + 63) / 64;
+  const int64_t xblocks = (dims->dim + 64 * kStepCh - 1) / (64 * kStepCh);
   if (xblocks > 0x7fffffffLL || dims->batch > 65535) return MAMBA_ERR_SHAPE;
   const dim3 grid((unsigned)xblocks, (unsigned)dims->batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
