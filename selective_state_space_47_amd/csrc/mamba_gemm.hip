@@ -1,16 +1,14 @@
-// mamba_gemm.hip -- bf16 MFMA GEMM for gfx950 (see mamba_gemm.h).
+// mamba_gemm.hip -- bf16 MFMA GEMMs for gfx950 (see mamba_gemm.h).
 //
-// Workgroup tile 128 x 128 (M x N), K step 64, 256 threads = 4 waves in a 2 x 2 grid, each wave
-// 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 64 registers); the tile
-// shape is a template (TileShape) so that other shapes can be measured.
-// Operand layouts of that instruction on gfx950 (checked with an in-bounds probe): lane l holds
-// A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; accumulator element i of lane l is
-// C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
-// Both operand tiles live in LDS with K contiguous, rows padded by 16 bytes (pitch 144 bytes: the
-// 16-byte fragment reads of 8 consecutive rows hit all 32 banks), double buffered:
-// the next K step is loaded into registers while the current one is multiplied.
-// An N-contiguous B tile is transposed in registers on its way to LDS (4 k-rows x 8 columns per
-// thread, packed into 8-byte column pieces).
+// gemm_big_kernel: both operands K-contiguous, 256 x 256 (or 256 x 128) workgroup tiles, one
+// wave per SIMD with 128 x 128 of accumulators, operands loaded straight into an LDS ring with
+// global_load_lds_dwordx4.  gemm_kernel: everything else (N-contiguous B, small M or K), 128 x 128
+// tiles with register-staged loads.  Details at each kernel.
+// Operand layouts of v_mfma_f32_32x32x16_bf16 on gfx950 (checked with an in-bounds probe): lane l
+// holds A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; accumulator element i of lane
+// l is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+#include <type_traits>
+
 #include "mamba_gemm.h"
 
 namespace mamba {
@@ -148,6 +146,13 @@ __device__ __forceinline__ void tile_of(const GemmArgs& p, int64_t w, int64_t* b
   *nt = tg / gm;
 }
 
+// Register-staged kernel.  Workgroup tile 128 x 128, K step 64, 256 threads = 4 waves in a 2 x 2
+// grid, each wave 2 x 2 MFMA tiles (fp32 accumulators, 64 registers).  Both operand tiles live in
+// LDS with K contiguous, rows padded by 16 bytes (pitch 144 bytes: the 16-byte fragment reads of
+// 8 consecutive rows hit all 32 banks of a 128-byte cycle), double buffered: the next K step is
+// loaded into registers while the current one is multiplied.  An N-contiguous B tile is
+// transposed in registers on its way to LDS (4 k-rows x 8 columns per thread, packed into 8-byte
+// column pieces).
 template <int kWM, int kWN, int kBK, bool kBKc>
 __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(GemmArgs p) {
   using S = TileShape<kWM, kWN, kBK>;
@@ -203,36 +208,41 @@ __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(Ge
     }
   }
 
-  // ---- epilogue: route rows to their destination, round to bf16
+  // ---- epilogue: round to bf16 and route rows to their destination.  The destinations are
+  // visited in an unrolled loop with constant indices, so their fields stay scalar; choosing a
+  // destination per lane instead makes the compiler index a private copy of the argument (one
+  // vector load per store, whose wait also waits for every earlier store).
 #pragma unroll
-  for (int i = 0; i < kWM; ++i) {
+  for (int di = 0; di < 3; ++di) {
+    if (di >= p.ndst) break;
+    const GemmDest& d = p.dst[di];
+    if (d.ptr == nullptr) continue;
+    uint16_t* base = d.ptr + bidx * d.bstride;
 #pragma unroll
-    for (int j = 0; j < kWN; ++j) {
-      const int64_t n = th.n0 + S::TN / 2 * wn + 32 * j + (lane & 31);
+    for (int i = 0; i < kWM; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // rows mq .. mq+3 of this lane (4 consecutive rows, inside one destination)
-        const int64_t mq = th.m0 + S::TM / 2 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
-        if (mq >= p.M || n >= p.N) continue;
-        int di = 0;
-        while (di + 1 < p.ndst && mq >= p.dst[di].m1) ++di;
-        const GemmDest& d = p.dst[di];
-        if (d.ptr == nullptr || mq < d.m0 || mq >= d.m1) continue;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        uint16_t* base = d.ptr + bidx * d.bstride;
-        const int64_t r = mq - d.m0;
-        if (d.trans) {
-          const uint2 w2 =
-              make_uint2(pack_bf16(make_float2(v0, v1)), pack_bf16(make_float2(v2, v3)));
-          *reinterpret_cast<uint2*>(base + n * d.ld + r) = w2;
-        } else {
-          const uint32_t w01 = pack_bf16(make_float2(v0, v1));
-          const uint32_t w23 = pack_bf16(make_float2(v2, v3));
-          base[r * d.ld + n] = (uint16_t)(w01 & 0xffffu);
-          base[(r + 1) * d.ld + n] = (uint16_t)(w01 >> 16);
-          base[(r + 2) * d.ld + n] = (uint16_t)(w23 & 0xffffu);
-          base[(r + 3) * d.ld + n] = (uint16_t)(w23 >> 16);
+      for (int j = 0; j < kWN; ++j) {
+        const int64_t n = th.n0 + S::TN / 2 * wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // rows mq .. mq+3 of this lane (4 consecutive rows, inside one destination)
+          const int64_t mq = th.m0 + S::TM / 2 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
+          if (mq < d.m0 || mq >= d.m1 || n >= p.N) continue;
+          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+          const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+          const int64_t r = mq - d.m0;
+          if (d.trans) {
+            const uint2 w2 =
+                make_uint2(pack_bf16(make_float2(v0, v1)), pack_bf16(make_float2(v2, v3)));
+            *reinterpret_cast<uint2*>(base + n * d.ld + r) = w2;
+          } else {
+            const uint32_t w01 = pack_bf16(make_float2(v0, v1));
+            const uint32_t w23 = pack_bf16(make_float2(v2, v3));
+            base[r * d.ld + n] = (uint16_t)(w01 & 0xffffu);
+            base[(r + 1) * d.ld + n] = (uint16_t)(w01 >> 16);
+            base[(r + 2) * d.ld + n] = (uint16_t)(w23 & 0xffffu);
+            base[(r + 3) * d.ld + n] = (uint16_t)(w23 >> 16);
+          }
         }
       }
     }
@@ -253,6 +263,336 @@ int launch_shape(const GemmArgs& a0, bool b_kcontig, int64_t batch, hipStream_t 
     hipLaunchKernelGGL((gemm_kernel<kWM, kWN, kBK, true>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((gemm_kernel<kWM, kWN, kBK, false>), grid, dim3(256), 0, s, a);
+  return launch_status();
+}
+
+// ------------------------------------------------------------------ large-tile kernel
+// Workgroup tile 256 x kTN (kTN = 256 or 128), 4 waves in a 2 x 2 grid, each wave
+// 128 x kTN/2 = 4 x kTN/64 MFMA tiles (up to 256 accumulator registers: one wave per SIMD).
+// Both operands must be K-contiguous.  They go from global memory straight into LDS with
+// global_load_lds_dwordx4 (lane L of a wave's load writes 16 bytes at M0 + 16 L, checked with an
+// in-bounds probe) through a ring of kS stages of kBK along K: the loads of step k + kS are issued
+// right after the barrier inside step k, so each load has kS - 1 steps of MFMA work to land.
+// The loads are issued from a short asm block (no output registers; it saves and restores M0):
+// the compiler's own wait placement for the builtin cannot tell the stage being read from the
+// stages being filled and waits for every load before each LDS read, which would serialise the
+// pipeline.  The kernel counts its own loads and waits once per step, before the barrier.
+// An operand stage is rows x kBK/8 words of 16 bytes.  gfx950 serves 16 lanes of a 16-byte LDS
+// read per cycle (256 bytes, 64 banks; measured: the 8-lane layout left 48% of LDS cycles in bank
+// conflicts), so word kw of row r is kept at slot kw ^ row_key(r), which puts the 16 rows that one
+// pass of a fragment read touches at 16 different 16-byte positions of a 256-byte bank cycle.  A
+// load instruction still reads whole row segments from memory.
+// Fragments are read one 16-deep K slice ahead of the MFMAs that use them (two register sets).
+// The last slice of a step is where the step ends: its fragments are waited for together with the
+// next stage's loads, then the barrier, the loads kS steps ahead (into the stage just finished)
+// and the next step's first fragments are issued, and only then the last slice's MFMAs.
+// Epilogue: each wave converts its accumulators to bf16 and stages them in LDS so that every
+// lane ends up storing 16 contiguous bytes of the destination.  With kSwap the MFMA is given
+// (B, A), so each lane holds 4 consecutive columns n of one row: the layout of a row-major
+// destination; without it each lane holds 4 consecutive rows m: a transposed destination.
+template <int kTN, int kBK, int kS>
+struct BigShape {
+  static constexpr int TM = 256, TN = kTN, BK = kBK, NS = kS;
+  static constexpr int FM = 4;              // 32-row MFMA tiles per wave
+  static constexpr int FN = kTN / 64;       // 32-column MFMA tiles per wave
+  static constexpr int KK = kBK / 16;       // 16-deep slices per step
+  static constexpr int WPR = kBK / 8;       // 16-byte words per row
+  static constexpr int RPI = 64 / WPR;      // rows per load instruction (one wave)
+  static constexpr int RP = 256 / (kBK * 2);  // rows per 256-byte bank cycle
+  static constexpr int PA = TM / 4 / RPI;   // load instructions per wave and step, A
+  static constexpr int PB = TN / 4 / RPI;   // and B
+  static constexpr int D = PA + PB;         // per wave and step
+  static constexpr int kStage = (TM + TN) * WPR;  // 16-byte words per stage
+  static constexpr int kEpi = 4 * 128 * (kTN / 2) * 2 / 16;  // words of the epilogue tiles
+  static constexpr int kSmem = kS * kStage > kEpi ? kS * kStage : kEpi;
+  static_assert(kTN == 256 || kTN == 128, "tile width");
+  static_assert(kBK == 32 || kBK == 64, "K step");
+  static_assert(kS >= 2 && (kS - 1) * D <= 63, "stages (the wait counter holds 63)");
+  // slot key of tile row r (rows r and r' of one pass: same r % RP, different r / RP)
+  __device__ static __forceinline__ int row_key(int r) { return (r / RP) % WPR; }
+};
+
+// One 16-byte load per lane from sbase + voff into LDS at lds_addr + 16 lane.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
+// at most kN of this wave's vector-memory operations are still outstanding (kN <= 63)
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
+}
+// wait_vm<c * kD> for a count c in [0, kMax] known only at run time (uniform)
+template <int kD, int kMax>
+__device__ __forceinline__ void wait_vm_steps(int c) {
+  if (kMax >= 4 && c >= 4) { wait_vm<(kMax >= 4 ? 4 * kD : 0)>(); return; }
+  if (kMax >= 3 && c == 3) { wait_vm<(kMax >= 3 ? 3 * kD : 0)>(); return; }
+  if (kMax >= 2 && c == 2) { wait_vm<(kMax >= 2 ? 2 * kD : 0)>(); return; }
+  if (kMax >= 1 && c == 1) { wait_vm<kD>(); return; }
+  wait_vm<0>();
+}
+
+// every wave of the workgroup has reached this point, with its LDS reads complete
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// a value the compiler may hold in VGPRs (it is computed with VALU division) moved to SGPRs
+__device__ __forceinline__ const uint16_t* to_sgpr(const uint16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  // the builtin returns int: widen through uint32_t, or a low word >= 2^31 sign-extends into the
+  // high word
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t*>((hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+template <int kTN, bool kSwap, int kBK, int kS>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs p) {
+  using S = BigShape<kTN, kBK, kS>;
+  __shared__ uint4 smem[S::kSmem];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  int64_t bidx, mt, nt;
+  tile_of(p, blockIdx.x, &bidx, &mt, &nt);
+  const int64_t m0 = mt * S::TM, n0 = nt * S::TN;
+  const uint16_t* Ab = to_sgpr(p.A + m0 * p.lda);
+  const uint16_t* Bb = to_sgpr(p.B + bidx * p.b_bstride + n0 * p.ldb);
+
+  // Per-lane byte offsets of the rows this lane loads (wave w, instruction j: tile rows
+  // RPI (w P + j) + lane / WPR, slot lane % WPR); rows past the matrix read its last row, whose
+  // products only reach rows or columns of C that are never stored.
+  uint32_t offa[S::PA], offb[S::PB];
+  {
+    const int rl = lane / S::WPR, sl = lane % S::WPR;
+#pragma unroll
+    for (int j = 0; j < S::PA; ++j) {
+      const int rt = S::RPI * (w * S::PA + j) + rl;
+      const int kw = sl ^ S::row_key(rt);
+      const int64_t r = min((int64_t)rt, p.M - 1 - m0);
+      offa[j] = (uint32_t)((r * p.lda + 8 * kw) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < S::PB; ++j) {
+      const int rt = S::RPI * (w * S::PB + j) + rl;
+      const int kw = sl ^ S::row_key(rt);
+      const int64_t r = min((int64_t)rt, p.N - 1 - n0);
+      offb[j] = (uint32_t)((r * p.ldb + 8 * kw) * 2);
+    }
+  }
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto load = [&](int st, int64_t k0) {
+    const uint32_t la = lds0 + st * S::kStage * 16 + w * S::PA * 1024;
+    const uint32_t lb = lds0 + st * S::kStage * 16 + S::TM * S::WPR * 16 + w * S::PB * 1024;
+    const uint16_t* ga = Ab + k0;
+    const uint16_t* gb = Bb + k0;
+#pragma unroll
+    for (int j = 0; j < S::PA; ++j) dma16(ga, offa[j], la + j * 1024);
+#pragma unroll
+    for (int j = 0; j < S::PB; ++j) dma16(gb, offb[j], lb + j * 1024);
+  };
+
+  f32x16_t acc[S::FM][S::FN];
+#pragma unroll
+  for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  bf16x8_t fa[2][S::FM], fb[2][S::FN];
+  auto read_frags = [&](int st, int kk, int buf) {
+    const uint4* sa = smem + st * S::kStage;
+    const uint4* sb = sa + S::TM * S::WPR;
+    // tile rows 128 wm + 32 i + (lane & 31): the key depends on lane & 31 alone
+    const int slot = (2 * kk + (lane >> 5)) ^ S::row_key(lane & 31);
+#pragma unroll
+    for (int i = 0; i < S::FM; ++i)
+      fa[buf][i] = __builtin_bit_cast(
+          bf16x8_t, sa[(128 * wm + 32 * i + (lane & 31)) * S::WPR + slot]);
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j)
+      fb[buf][j] = __builtin_bit_cast(
+          bf16x8_t, sb[(S::TN / 2 * wn + 32 * j + (lane & 31)) * S::WPR + slot]);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j)
+        acc[i][j] = kSwap
+            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0)
+            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // slices 0 .. KK-2 of the step in stage st (slice 0's fragments are already in set 0)
+  auto first_slices = [&](int st) {
+#pragma unroll
+    for (int kk = 0; kk + 1 < S::KK; ++kk) {
+      read_frags(st, kk + 1, (kk + 1) & 1);
+      mfmas(kk & 1);
+    }
+  };
+
+  const int nk = __builtin_amdgcn_readfirstlane((int)(p.K / S::BK));
+  // prologue: steps 0 .. kS-1 into stages 0 .. kS-1; wait for step 0
+  for (int st = 0; st < kS && st < nk; ++st) load(st, (int64_t)st * S::BK);
+  wait_vm_steps<S::D, kS - 1>(min(kS - 1, nk - 1));
+  lds_barrier();
+  read_frags(0, 0, 0);
+  // One step ks (stage st) except its last slice's MFMAs, then the barrier that hands over to
+  // step ks + 1, then the last slice's MFMAs with the loads of step ks + kS (into stage st, just
+  // released) spread between them, one per kMfmaPerLoad MFMAs, so that no burst of load issues
+  // holds back the matrix cores.
+  constexpr int kMfmas = S::FM * S::FN;
+  constexpr int kMfmaPerLoad = kMfmas / S::D > 0 ? kMfmas / S::D : 1;
+  auto step = [&](int ks, int st, auto with_loads) {
+    first_slices(st);
+    // step ks + 1 must have landed; loads of steps ks + 2 .. min(ks + kS - 1, nk - 1) may fly
+    wait_vm_steps<S::D, kS - 2>(min(kS - 2, nk - 2 - ks));
+    lds_barrier();  // every wave has step ks + 1 in LDS and is done reading step ks
+    const int st1 = st + 1 == kS ? 0 : st + 1;
+    read_frags(st1, 0, 0);
+    constexpr int buf = (S::KK - 1) & 1;
+    const uint32_t la = lds0 + st * S::kStage * 16 + w * S::PA * 1024;
+    const uint32_t lb = lds0 + st * S::kStage * 16 + S::TM * S::WPR * 16 + w * S::PB * 1024;
+    const int64_t k0 = (int64_t)(ks + kS) * S::BK;
+#pragma unroll
+    for (int x = 0; x < kMfmas; ++x) {
+      const int i = x / S::FN, j = x % S::FN;
+      acc[i][j] = kSwap
+          ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0)
+          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      if (decltype(with_loads)::value && x % kMfmaPerLoad == kMfmaPerLoad - 1) {
+        const int l = x / kMfmaPerLoad;
+        if (l < S::PA) dma16(Ab + k0, offa[l], la + l * 1024);
+        else if (l < S::D) dma16(Bb + k0, offb[l - S::PA], lb + (l - S::PA) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (decltype(with_loads)::value) {  // loads left over when there are more than MFMAs
+#pragma unroll
+      for (int l = kMfmas / kMfmaPerLoad; l < S::D; ++l) {
+        if (l < S::PA) dma16(Ab + k0, offa[l], la + l * 1024);
+        else dma16(Bb + k0, offb[l - S::PA], lb + (l - S::PA) * 1024);
+      }
+    }
+    return st1;
+  };
+  int st = 0, ks = 0;
+  for (; ks + kS < nk; ++ks) st = step(ks, st, std::true_type{});
+  for (; ks + 1 < nk; ++ks) st = step(ks, st, std::false_type{});
+  first_slices(st);  // the last step
+  mfmas((S::KK - 1) & 1);
+  lds_barrier();  // every wave is done with the stages; they now hold the epilogue tiles
+
+  // ---- epilogue.  E: this wave's tile, rows = the second MFMA operand's index (m with kSwap,
+  // n without), columns = the first operand's (contiguous in the destination), bf16.  An 8-byte
+  // piece c8 of row r is kept at slot c8 ^ (r & 15): the 16 lanes of one write pass (16 rows,
+  // the same piece) hit 16 different 8-byte bank pairs.
+  constexpr int F1 = kSwap ? S::TN / 2 : 128;  // columns of E
+  constexpr int F2 = kSwap ? 128 : S::TN / 2;  // rows of E
+  constexpr int kPitch = F1 * 2;               // bytes per row
+  uint8_t* E = reinterpret_cast<uint8_t*>(smem) + w * (F1 * F2 * 2);
+#pragma unroll
+  for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j) {
+      const int t1 = kSwap ? j : i, t2 = kSwap ? i : j;
+      const int r = 32 * t2 + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c8 = 8 * t1 + 2 * g + (lane >> 5);
+        const uint2 v = make_uint2(
+            pack_bf16(make_float2(acc[i][j][4 * g], acc[i][j][4 * g + 1])),
+            pack_bf16(make_float2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])));
+        *reinterpret_cast<uint2*>(E + r * kPitch + ((c8 ^ (r & 15)) * 8)) = v;
+      }
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave reads back what it wrote
+  // The whole tile lies in one destination (the launcher only takes calls whose destination
+  // boundaries are multiples of the tile height); it is chosen with uniform branches and
+  // constant indices, so its fields stay scalar.
+  auto store_tile = [&](const GemmDest& d) {
+    if (d.ptr == nullptr) return;
+    uint16_t* base = d.ptr + bidx * d.bstride;
+    constexpr int kChunks = kPitch / 16;       // 16-byte chunks per row of E
+    constexpr int kRowsPerPass = 64 / kChunks;
+    const int q = lane % kChunks;
+#pragma unroll
+    for (int it = 0; it < F2 / kRowsPerPass; ++it) {
+      const int r = it * kRowsPerPass + lane / kChunks;
+      uint4 v = *reinterpret_cast<const uint4*>(E + r * kPitch + ((q ^ ((r & 15) >> 1)) * 16));
+      if (r & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      int64_t m, n;
+      if (kSwap) {
+        m = m0 + 128 * wm + r;
+        n = n0 + S::TN / 2 * wn + 8 * q;
+      } else {
+        n = n0 + S::TN / 2 * wn + r;
+        m = m0 + 128 * wm + 8 * q;
+      }
+      if (m >= p.M || n >= p.N) continue;
+      const int64_t off = kSwap ? (m - d.m0) * d.ld + n : n * d.ld + (m - d.m0);
+      *reinterpret_cast<uint4*>(base + off) = v;
+    }
+  };
+  if (p.ndst > 2 && m0 >= p.dst[1].m1) store_tile(p.dst[2]);
+  else if (p.ndst > 1 && m0 >= p.dst[0].m1) store_tile(p.dst[1]);
+  else store_tile(p.dst[0]);
+}
+
+// imbalance of t equal tiles over the CUs: the busiest CU's share over the mean
+double tile_imbalance(int64_t t) {
+  const int64_t cus = 256;
+  const int64_t rounds = (t + cus - 1) / cus;
+  return (double)(rounds * cus) / (double)t;
+}
+
+// K step and stage count of the large-tile kernel
+constexpr int kBigBK = 32, kBigStages = 5;
+
+// Whether the large-tile kernel serves this call: B K-contiguous, K a multiple of 64, M at least
+// one tile, and destinations that take 16-byte stores (one orientation for all of them).
+bool big_ok(const GemmArgs& a, bool b_kcontig) {
+  if (!b_kcontig || a.K % 64 || a.M < 256 || a.N < 128) return false;
+  for (int i = 0; i < a.ndst; ++i) {
+    const GemmDest& d = a.dst[i];
+    if (d.trans != a.dst[0].trans) return false;
+    if (i + 1 < a.ndst && d.m1 % 256) return false;  // a tile must lie in one destination
+    if (d.ptr && (!aligned(d.ptr, 16) || d.ld % 8 || d.bstride % 8)) return false;
+  }
+  return true;
+}
+
+template <int kTN, int kBK, int kS>
+int launch_big(const GemmArgs& a0, int64_t batch, hipStream_t s) {
+  using S = BigShape<kTN, kBK, kS>;
+  GemmArgs a = a0;
+  a.mtiles = (int32_t)((a.M + S::TM - 1) / S::TM);
+  a.ntiles = (int32_t)((a.N + S::TN - 1) / S::TN);
+  a.batch = batch;
+  if ((int64_t)a.mtiles * a.ntiles * batch > 0x7fffffffLL || batch > 65535 || batch < 1)
+    return MAMBA_ERR_SHAPE;
+  const dim3 grid((unsigned)((int64_t)a.mtiles * a.ntiles * batch));
+  if (a.dst[0].trans)
+    hipLaunchKernelGGL((gemm_big_kernel<kTN, false, kBK, kS>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<kTN, true, kBK, kS>), grid, dim3(256), 0, s, a);
   return launch_status();
 }
 
@@ -280,6 +620,14 @@ int launch_gemm(const GemmArgs& a, bool b_kcontig, int64_t batch, hipStream_t s)
   // 256 x 256 x 32 (one workgroup per CU, 4 x 4 tiles per wave in AGPRs) and 128 x 256 x 32 were
   // 10-25% slower: with register staging the per-step wait for the next tile's loads, its LDS
   // store and the barrier dominate, and shallower K steps pay them more often.
+  if (big_ok(a, b_kcontig)) {
+    const int64_t mt = (a.M + 255) / 256;
+    const int64_t t256 = mt * ((a.N + 255) / 256) * batch;
+    const int64_t t128 = mt * ((a.N + 127) / 128) * batch;
+    if (tile_imbalance(t256) <= tile_imbalance(t128) * 1.05)
+      return launch_big<256, kBigBK, kBigStages>(a, batch, s);
+    return launch_big<128, kBigBK, kBigStages>(a, batch, s);
+  }
   return launch_shape<2, 2, 64>(a, b_kcontig, batch, s);
 }
 
