@@ -96,6 +96,10 @@ size_t mamba_scan_workspace_bytes(const mamba_dims* dims);
  *
  * NULL allowed for D (no skip), z (no gate), delta_bias (zero bias), last_state (not written).
  * softplus_flag != 0 applies softplus to delta_raw + bias.
+ * seqlen * 32 * sizeof(io element) must stay below 2^32 (seqlen < 2^25 in fp32, 2^26 in bf16;
+ * MAMBA_ERR_SHAPE otherwise): a workgroup addresses its 32 channel rows with 32-bit offsets.
+ * The same bound applies to every entry point that runs the forward scan (the fused-conv forward,
+ * the backward's recomputation and the block).
  */
 int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, int softplus_flag,

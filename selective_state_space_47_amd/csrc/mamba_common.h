@@ -51,6 +51,16 @@ __device__ __forceinline__ float2 load_pair(const float* p, int64_t i, bool ok0,
   return make_float2(ok0 ? p[i] : 0.f, ok1 ? p[i + 1] : 0.f);
 }
 
+// base + a byte offset (a scalar base and a 32-bit lane offset map to scalar-base addressing)
+template <typename T>
+__device__ __forceinline__ const T* at(const T* base, uint32_t byte_off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -235,6 +245,9 @@ inline int check_dims(const mamba_dims* dm, bool step) {
   if ((double)dm->batch * (double)dm->dim * (double)dm->seqlen > (double)lim)
     return MAMBA_ERR_SHAPE;
   if (!step && (dm->chunk_len < 0 || dm->chunk_len % kChunkAlign != 0)) return MAMBA_ERR_SHAPE;
+  // the forward kernels address a workgroup's kChWG channel rows with 32-bit byte offsets
+  const int64_t esize = dm->io_dtype == MAMBA_BF16 ? 2 : 4;
+  if (!step && dm->seqlen * kChWG * esize >= ((int64_t)1 << 32)) return MAMBA_ERR_SHAPE;
   return MAMBA_OK;
 }
 

@@ -61,16 +61,22 @@ struct ScanThread {
   static constexpr bool kMain = kMode == kModeMain;
   using Raw = typename RawPair<Tin>::T;
   ScanSmem& sm;
+  // u, Delta_raw, z and out are addressed as a base shared by the workgroup (its first
+  // channel's row; scalar registers) plus this lane's 32-bit byte offset lofs (its channel's row
+  // and token pair), so loads and stores use scalar-base addressing with the sub-tile as an
+  // immediate offset
   const Tin* __restrict__ U;
   const Tin* __restrict__ DL;
   const Tin* __restrict__ Z;
   Tin* __restrict__ O;
+  uint32_t lofs;
   float* __restrict__ CK;  // checkpoint row of this lane's channel, offset by 2g
-  const Tin* __restrict__ BC0;  // B row 2*bg of the sequence (row 2*bg+1 follows at +L)
-  const Tin* __restrict__ CC0;  // C row 2*bg
+  const Tin* __restrict__ Bs;  // B and C of the sequence (workgroup bases; rows 2bg, 2bg+1 at
+  const Tin* __restrict__ Cs;  // the lane offset bofs and bofs + L)
+  uint32_t bofs;
   int w, lane, c, g, btp, bg;
   bool dvalid;
-  int64_t row, t_end, row_stride_L;
+  int64_t t_end, L;
   float a0, a1, bias, dskip;
   float h0 = 0.f, h1 = 0.f, dsum = 0.f;
   float cw0, cw1, cw2, cw3, cbias;  // conv taps, oldest first, and bias (kConv)
@@ -92,9 +98,9 @@ struct ScanThread {
       ok0 = 2 * g < rem;
       ok1 = 2 * g + 1 < rem;
     }
-    ru[s] = load_pair<kVec>(U, row + t, ok0, ok1);
-    rd[s] = load_pair<kVec>(DL, row + t, ok0, ok1);
-    if (kGate) rz[s] = load_pair<kVec>(Z, row + t, ok0, ok1);
+    ru[s] = load_pair<kVec>(at(U + tb, lofs), 0, ok0, ok1);
+    rd[s] = load_pair<kVec>(at(DL + tb, lofs), 0, ok0, ok1);
+    if (kGate) rz[s] = load_pair<kVec>(at(Z + tb, lofs), 0, ok0, ok1);
   }
   // B/C staging loads: thread -> token pair btp (0..31) of the tile, lane group bg (0..7); it
   // loads the pairs of rows 2bg, 2bg+1 of B and of C and later writes the two float4s of its
@@ -102,10 +108,10 @@ struct ScanThread {
   __device__ __forceinline__ void load_bc(int64_t t0) {
     const int64_t t = t0 + 2 * btp;
     const bool ok0 = t < t_end, ok1 = t + 1 < t_end;
-    rbc[0] = load_pair<kVec>(BC0, t, ok0, ok1);
-    rbc[1] = load_pair<kVec>(BC0 + row_stride_L, t, ok0, ok1);
-    rbc[2] = load_pair<kVec>(CC0, t, ok0, ok1);
-    rbc[3] = load_pair<kVec>(CC0 + row_stride_L, t, ok0, ok1);
+    rbc[0] = load_pair<kVec>(at(Bs + t0, bofs), 0, ok0, ok1);
+    rbc[1] = load_pair<kVec>(at(Bs + L + t0, bofs), 0, ok0, ok1);
+    rbc[2] = load_pair<kVec>(at(Cs + t0, bofs), 0, ok0, ok1);
+    rbc[3] = load_pair<kVec>(at(Cs + L + t0, bofs), 0, ok0, ok1);
   }
   // prefetch of sub-tile s of the tile starting at tn (uniform branch)
   __device__ __forceinline__ void prefetch_sub(int64_t tn, int s) {
@@ -134,7 +140,8 @@ struct ScanThread {
 
   // One 64-token tile starting at t0 (kFull: all of it inside the chunk); prefetches the tile
   // starting at t0 + kTT when that starts before t_end.
-  template <bool kFull>
+  // kNextFull: the tile at t0 + kTT is whole too (no test before its prefetch)
+  template <bool kFull, bool kNextFull>
   __device__ __forceinline__ void tile(int64_t t0) {
     const int64_t tn = t0 + kTT;
     __syncthreads();  // every wave is done reading the previous tile's B/C
@@ -144,7 +151,7 @@ struct ScanThread {
       sm.bc[2 * btp][bg] = make_float4(b0.x, b1.x, c0.x, c1.x);
       sm.bc[2 * btp + 1][bg] = make_float4(b0.y, b1.y, c0.y, c1.y);
     }
-    if (tn < t_end) load_bc(tn);
+    if (kNextFull || tn < t_end) load_bc(tn);
     __syncthreads();
 
 #pragma unroll
@@ -161,12 +168,13 @@ struct ScanThread {
       float2 x = unpack(ru[s]);
       if (kConv) {
         x = conv_pair(x);
-        if (kMain && UO) store_pair<kVec>(UO, row + tp, x, dvalid && ok0, dvalid && ok1);
+        if (kMain && UO) store_pair<kVec>(at(UO + tb, lofs), 0, x, dvalid && ok0, dvalid && ok1);
       }
       const float2 dr = unpack(rd[s]);
       float2 zz;
       if (kGate) zz = unpack(rz[s]);
-      prefetch_sub(tn, s);
+      if (kNextFull) load_sub<true>(tn + kTS * s, s);
+      else prefetch_sub(tn, s);
       float dl0 = dr.x + bias, dl1 = dr.y + bias;
       if (kSoftplus) {
         dl0 = softplus_f32(dl0);
@@ -224,7 +232,7 @@ struct ScanThread {
           y.x *= silu_f32(zz.x);
           y.y *= silu_f32(zz.y);
         }
-        store_pair<kVec>(O, row + tp, y, dvalid && ok0, dvalid && ok1);
+        store_pair<kVec>(at(O + tb, lofs), 0, y, dvalid && ok0, dvalid && ok1);
       }
       wave_lds_fence();
       __builtin_amdgcn_sched_barrier(0);
@@ -260,7 +268,15 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   th.dvalid = d < p.dim;
   const int64_t dd_ = th.dvalid ? d : (cb - b * p.dblocks) * kChWG;
   const int64_t ch = b * p.dim + dd_;
-  th.row = ch * p.L;
+  // workgroup bases (the block's first channel) and this lane's offset from them; the host
+  // keeps kChWG * L * sizeof(Tin) below 2^32
+  const int64_t ch0 = b * p.dim + (cb - b * p.dblocks) * kChWG;
+  th.U += ch0 * p.L;
+  th.DL += ch0 * p.L;
+  th.Z += ch0 * p.L;
+  th.O += ch0 * p.L;
+  th.lofs = (uint32_t)(((ch - ch0) * p.L + 2 * g) * (int64_t)sizeof(Tin));
+  th.L = p.L;
   if (kMode == kModeCkpt) th.CK = p.ckpt + ch * p.nblk8 * kN + 2 * g;
   const int64_t t_begin = k * p.chunk_len;
   th.t_end = min(p.L, t_begin + p.chunk_len);
@@ -278,10 +294,10 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
     th.cw2 = W >= 2 ? wr[W - 2] : 0.f;
     th.cw3 = wr[W - 1];
     th.cbias = p.conv_b ? p.conv_b[dd_] : 0.f;
-    th.UO = static_cast<Tin*>(p.u_out);
+    th.UO = p.u_out ? static_cast<Tin*>(p.u_out) + ch0 * p.L : nullptr;
     // the last pair of each lane in the 16 tokens before the chunk (zero before the sequence)
     if (t_begin >= kTS) {
-      const float2 v = unpack(load_pair<kVec>(th.U, th.row + t_begin - kTS + 2 * g, true, true));
+      const float2 v = unpack(load_pair<kVec>(at(th.U + (t_begin - kTS), th.lofs), 0, true, true));
       th.px0 = v.x;
       th.px1 = v.y;
     }
@@ -305,9 +321,9 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   // B/C staging assignment: thread -> (token pair 8w + lane/8 of the tile, lane group lane%8)
   th.btp = 8 * th.w + (th.lane >> 3);
   th.bg = th.lane & 7;
-  th.row_stride_L = p.L;
-  th.BC0 = Bm + (b * kN + 2 * th.bg) * p.L;
-  th.CC0 = Cm + (b * kN + 2 * th.bg) * p.L;
+  th.Bs = Bm + b * kN * p.L;
+  th.Cs = Cm + b * kN * p.L;
+  th.bofs = (uint32_t)((2 * th.bg * p.L + 2 * th.btp) * (int64_t)sizeof(Tin));
 
   // raw registers are prefetched one tile ahead: sub-tile s of the next tile is loaded as soon
   // as sub-tile s of the current tile has consumed its registers, B/C right after staging
@@ -321,8 +337,13 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   }
   th.load_bc(t_begin);
   int64_t t0 = t_begin;
-  for (; t0 + kTT <= t_end; t0 += kTT) th.template tile<true>(t0);
-  if (t0 < t_end) th.template tile<false>(t0);
+  // steady state: this tile and the next are whole, so the prefetch needs no test
+  for (; t0 + 2 * kTT <= t_end; t0 += kTT) th.template tile<true, true>(t0);
+  if (t0 + kTT <= t_end) {
+    th.template tile<true, false>(t0);
+    t0 += kTT;
+  }
+  if (t0 < t_end) th.template tile<false, false>(t0);
 
   if (kMode == kModeMain) {
     if (p.last_state && th.dvalid && k == p.nchunks - 1) {

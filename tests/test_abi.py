@@ -70,6 +70,10 @@ def test_scan_validation_codes(lib):
     assert call_scan(lib, dims(io=7)) == -3
     assert call_scan(lib, dims(chunk=24)) == -2
     assert call_scan(lib, dims(chunk=-16)) == -2
+    # 32 channel rows of a workgroup are addressed with 32-bit byte offsets
+    assert call_scan(lib, dims(batch=1, dim=1, seqlen=1 << 25)) == -2            # fp32
+    assert call_scan(lib, dims(batch=1, dim=1, seqlen=1 << 26, io=1)) == -2      # bf16
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(dims(batch=1, dim=1, seqlen=1 << 25))) == 0
     assert call_scan(lib, dims(), u=ODD) == -5
     assert call_scan(lib, dims(io=1), z=ODD) == -5
     # chunked plan needs a workspace
