@@ -14,9 +14,10 @@
 //   3. x_proj    (MFMA GEMM): [Delta_low; B; C] ((R + 2N) x L) = W_x * u; rows are routed to
 //                 three buffers, B and C in the (N, L) layout of the scan.
 //   4. dt_proj   (MFMA GEMM): Delta_raw (E x L) = W_dt (E x R) * Delta_low.
-//   5. scan      y = selective_scan(u, Delta_raw, A, B, C, D, z, dt_bias, softplus).
-//   6. out_proj  (MFMA GEMM): out (L x d_model) = (W_out (d_model x E) * y)^T, stored token-major
-//                 by the transposing epilogue.
+//   5. scan      y = selective_scan(u, Delta_raw, A, B, C, D, z, dt_bias, softplus); y is stored
+//                 token-major (L, E) so that out_proj contracts over its contiguous axis.
+//   6. out_proj  (MFMA GEMM): out (L x d_model) = (W_out (d_model x E) * y)^T, with both operands
+//                 K-contiguous, stored token-major by the transposing epilogue.
 // Intermediates are stored in bf16 (fp32 accumulation everywhere).
 #include "mamba_gemm.h"
 
@@ -208,22 +209,24 @@ int mamba_block_fwd(const void* hidden, const void* w_in, const float* conv_weig
   // 5. selective scan (softplus(Delta_raw + dt_bias), z gate, D skip), bf16 storage
   mamba_dims sd = {Bt, E, N, L, MAMBA_BF16, 0};
   const size_t scan_ws = lay.total - lay.scan;
-  st = mamba_scan_fwd(u, dt, A, bc, cc, D, z, dt_bias, 1, y, nullptr, &sd, ws + lay.scan,
-                      scan_ws, stream);
+  // y is stored token-major, (L, E) per sequence, so that out_proj contracts over its
+  // contiguous axis
+  st = scan_forward(u, nullptr, nullptr, 0, nullptr, dt, A, bc, cc, D, z, dt_bias, 1, y, nullptr,
+                    &sd, ws + lay.scan, scan_ws, stream, true);
   if (st != MAMBA_OK) return st;
 
-  // 6. out_proj: out (L, d_model) per sequence = (W_out * y)^T
+  // 6. out_proj: out (L, d_model) per sequence = (W_out * y)^T, with y K-contiguous
   g = GemmArgs{};
   g.A = static_cast<const uint16_t*>(w_out);
   g.lda = E;
   g.B = y;
-  g.ldb = L;
+  g.ldb = E;
   g.b_bstride = E * L;
   g.M = Dm; g.N = L; g.K = E;
   g.ndst = 1;
   g.dst[0] = {static_cast<uint16_t*>(out), 0, Dm, Dm, L * Dm, 1};
   if ((st = gemm_check(g)) != MAMBA_OK) return st;
-  return launch_gemm(g, false, Bt, s);
+  return launch_gemm(g, true, Bt, s);
 }
 
 }  // extern "C"

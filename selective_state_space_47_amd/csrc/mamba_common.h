@@ -221,6 +221,7 @@ struct ScanArgs {
 constexpr int kModeSummary = 0;  // chunk summary: local final state from zero and sum of Delta
 constexpr int kModeMain = 1;     // full forward: carry-in, readout, epilogue, last_state
 constexpr int kModeCkpt = 2;     // state before every 8th token, for the backward (no readout)
+constexpr int kModeMainT = 3;    // full forward with out stored token-major, (batch, L, dim)
 
 // ------------------------------------------------------------------ host: validation and plan
 
@@ -280,6 +281,12 @@ inline int launch_status() {
 }
 
 // Launches the forward kernel in `mode` (defined with the forward kernels).
+__attribute__((visibility("hidden"))) int scan_forward(
+    const void* u, const float* conv_w, const float* conv_b, int conv_width, void* u_out,
+    const void* delta, const float* A, const void* B, const void* C, const float* D,
+    const void* z, const float* delta_bias, int softplus_flag, void* out, float* last_state,
+    const mamba_dims* dims, void* workspace, size_t workspace_bytes, void* stream,
+    bool out_tmajor);
 __attribute__((visibility("hidden"))) int launch_fwd(int mode, bool bf, bool vec, bool softplus,
                                                      bool gate, dim3 grid, hipStream_t s,
                                                      const ScanArgs& a);

@@ -58,7 +58,8 @@ struct __align__(16) ScanSmem {
 //   prologue (width <= 4; narrower kernels are zero-padded at the oldest taps).
 template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate, bool kConv>
 struct ScanThread {
-  static constexpr bool kMain = kMode == kModeMain;
+  static constexpr bool kMain = kMode == kModeMain || kMode == kModeMainT;
+  static constexpr bool kOutT = kMode == kModeMainT;
   using Raw = typename RawPair<Tin>::T;
   ScanSmem& sm;
   // u, Delta_raw, z and out are addressed as a base shared by the workgroup (its first
@@ -70,6 +71,9 @@ struct ScanThread {
   const Tin* __restrict__ Z;
   Tin* __restrict__ O;
   uint32_t lofs;
+  Tin* __restrict__ OT;  // token-major output (kOutT): the wave's first channel at token 0
+  uint32_t lofsT;        // and this lane's byte offset from it (token 2g, channel c)
+  int64_t dim;
   float* __restrict__ CK;  // checkpoint row of this lane's channel, offset by 2g
   const Tin* __restrict__ Bs;  // B and C of the sequence (workgroup bases; rows 2bg, 2bg+1 at
   const Tin* __restrict__ Cs;  // the lane offset bofs and bofs + L)
@@ -232,7 +236,16 @@ struct ScanThread {
           y.x *= silu_f32(zz.x);
           y.y *= silu_f32(zz.y);
         }
-        store_pair<kVec>(at(O + tb, lofs), 0, y, dvalid && ok0, dvalid && ok1);
+        if (kOutT) {
+          // token-major output: lane (c, g) stores channel c of tokens 2g and 2g+1; the wave's
+          // 8 channels of one token are 16 contiguous bytes
+          const uint32_t pw = pack_bf16(y);
+          uint16_t* o = reinterpret_cast<uint16_t*>(at(OT + tb * dim, lofsT));
+          if (dvalid && ok0) o[0] = (uint16_t)(pw & 0xffffu);
+          if (dvalid && ok1) o[dim] = (uint16_t)(pw >> 16);
+        } else {
+          store_pair<kVec>(at(O + tb, lofs), 0, y, dvalid && ok0, dvalid && ok1);
+        }
       }
       wave_lds_fence();
       __builtin_amdgcn_sched_barrier(0);
@@ -242,7 +255,7 @@ struct ScanThread {
 
 template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate, bool kConv>
 __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
-  constexpr bool kMain = kMode == kModeMain;
+  constexpr bool kMain = kMode == kModeMain || kMode == kModeMainT;
   __shared__ ScanSmem sm;
   ScanThread<Tin, kMode, kVec, kSoftplus, kGate, kConv> th(sm);
   th.U = static_cast<const Tin*>(p.u);
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   const Tin* __restrict__ Cm = static_cast<const Tin*>(p.C);
 
   const int tid = threadIdx.x;
-  th.w = tid >> 6;
+  th.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   th.lane = tid & 63;
   th.c = th.lane >> 3;
   th.g = th.lane & 7;
@@ -277,6 +290,12 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   th.O += ch0 * p.L;
   th.lofs = (uint32_t)(((ch - ch0) * p.L + 2 * g) * (int64_t)sizeof(Tin));
   th.L = p.L;
+  if (kMode == kModeMainT) {
+    th.dim = p.dim;
+    th.OT = static_cast<Tin*>(p.out) + b * p.L * p.dim + (cb - b * p.dblocks) * kChWG +
+            th.w * kChW;
+    th.lofsT = (uint32_t)((2 * g * p.dim + th.c) * (int64_t)sizeof(Tin));
+  }
   if (kMode == kModeCkpt) th.CK = p.ckpt + ch * p.nblk8 * kN + 2 * g;
   const int64_t t_begin = k * p.chunk_len;
   th.t_end = min(p.L, t_begin + p.chunk_len);
@@ -345,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   }
   if (t0 < t_end) th.template tile<false, false>(t0);
 
-  if (kMode == kModeMain) {
+  if (kMain) {
     if (p.last_state && th.dvalid && k == p.nchunks - 1) {
       p.last_state[ch * kN + 2 * g] = th.h0;
       p.last_state[ch * kN + 2 * g + 1] = th.h1;
@@ -460,7 +479,8 @@ int launch_one(dim3 grid, hipStream_t s, const ScanArgs& a) {
 
 template <typename Tin, int kMode, bool kVec, bool kConv>
 int launch_flags(bool softplus, bool gate, dim3 grid, hipStream_t s, const ScanArgs& a) {
-  constexpr bool kG = kMode == kModeMain;  // only the main pass has a readout to gate
+  // only the main passes have a readout to gate
+  constexpr bool kG = kMode == kModeMain || kMode == kModeMainT;
   if (softplus)
     return gate ? launch_one<Tin, kMode, kVec, true, kG, kConv>(grid, s, a)
                 : launch_one<Tin, kMode, kVec, true, false, kConv>(grid, s, a);
@@ -471,7 +491,7 @@ int launch_flags(bool softplus, bool gate, dim3 grid, hipStream_t s, const ScanA
 template <int kMode, bool kConv>
 int launch_scan(bool bf, bool vec, bool softplus, bool gate, dim3 grid, hipStream_t s,
                 const ScanArgs& a) {
-  if (kMode != kModeMain) gate = false;
+  if (kMode != kModeMain && kMode != kModeMainT) gate = false;
   if (bf) return vec ? launch_flags<uint16_t, kMode, true, kConv>(softplus, gate, grid, s, a)
                      : launch_flags<uint16_t, kMode, false, kConv>(softplus, gate, grid, s, a);
   return vec ? launch_flags<float, kMode, true, kConv>(softplus, gate, grid, s, a)
@@ -493,6 +513,9 @@ int mamba::launch_fwd(int mode, bool bf, bool vec, bool softplus, bool gate, dim
     case kModeCkpt:
       return conv ? MAMBA_ERR_UNSUPPORTED
                   : launch_scan<kModeCkpt, false>(bf, vec, softplus, gate, grid, s, a);
+    case kModeMainT:  // bf16, vectorised, no conv (the block's layout)
+      if (conv || !bf || !vec) return MAMBA_ERR_UNSUPPORTED;
+      return launch_flags<uint16_t, kModeMainT, true, false>(softplus, gate, grid, s, a);
     default: return MAMBA_ERR_UNSUPPORTED;
   }
 }
@@ -500,11 +523,12 @@ int mamba::launch_fwd(int mode, bool bf, bool vec, bool softplus, bool gate, dim
 namespace mamba {
 
 // Forward, optionally with the fused conv (conv_w != NULL: `u` holds x).
+// out_tmajor: out is (batch, L, dim) (bf16, dim % 8 == 0, no conv; used by the block).
 int scan_forward(const void* u, const float* conv_w, const float* conv_b, int conv_width,
                  void* u_out, const void* delta, const float* A, const void* B, const void* C,
                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
                  void* out, float* last_state, const mamba_dims* dims, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 size_t workspace_bytes, void* stream, bool out_tmajor) {
   int st = check_dims(dims, false);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL;
@@ -547,8 +571,11 @@ int scan_forward(const void* u, const float* conv_w, const float* conv_b, int co
     if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
       return MAMBA_ERR_HIP;
   }
+  if (out_tmajor && (conv_w || !bf || !vec || dims->dim % 8 || !aligned(out, 16)))
+    return MAMBA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)(nwg_ch * pl.nchunks));
-  return launch_fwd(kModeMain, bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
+  return launch_fwd(out_tmajor ? kModeMainT : kModeMain, bf, vec, softplus_flag != 0,
+                    z != nullptr, grid, s, a);
 }
 
 }  // namespace mamba
@@ -569,7 +596,8 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    void* out, float* last_state, const mamba_dims* dims, void* workspace,
                    size_t workspace_bytes, void* stream) {
   return scan_forward(u, nullptr, nullptr, 0, nullptr, delta, A, B, C, D, z, delta_bias,
-                      softplus_flag, out, last_state, dims, workspace, workspace_bytes, stream);
+                      softplus_flag, out, last_state, dims, workspace, workspace_bytes, stream,
+                      false);
 }
 
 int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
@@ -582,7 +610,7 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
   if (conv_width < 1 || conv_width > 4) return MAMBA_ERR_UNSUPPORTED;
   return scan_forward(x, conv_weight, conv_bias, conv_width, u_out, delta, A, B, C, D, z,
                       delta_bias, softplus_flag, out, last_state, dims, workspace,
-                      workspace_bytes, stream);
+                      workspace_bytes, stream, false);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const float* A,
