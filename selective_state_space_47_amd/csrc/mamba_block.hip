@@ -12,8 +12,10 @@
 //                 x and z are written channel-major (E, L), the layout the scan reads.
 //   2. conv      u = silu(causal_conv1d(x) + conv_b) (channel-major, 8 tokens per thread).
 //   3. x_proj    (MFMA GEMM): [Delta_low; B; C] ((R + 2N) x L) = W_x * u; rows are routed to
-//                 three buffers, B and C in the (N, L) layout of the scan.
-//   4. dt_proj   (MFMA GEMM): Delta_raw (E x L) = W_dt (E x R) * Delta_low.
+//                 three buffers: Delta_low token-major (L, R), B and C in the (N, L) layout of
+//                 the scan.
+//   4. dt_proj   (MFMA GEMM): Delta_raw (E x L) = W_dt (E x R) * Delta_low, both operands
+//                 K-contiguous.
 //   5. scan      y = selective_scan(u, Delta_raw, A, B, C, D, z, dt_bias, softplus); y is stored
 //                 token-major (L, E) so that out_proj contracts over its contiguous axis.
 //   6. out_proj  (MFMA GEMM): out (L x d_model) = (W_out (d_model x E) * y)^T, with both operands
@@ -178,7 +180,8 @@ int mamba_block_fwd(const void* hidden, const void* w_in, const float* conv_weig
                      x, conv_weight, conv_bias, u, E, L, dims->conv_width, total8);
   if ((st = launch_status()) != MAMBA_OK) return st;
 
-  // 3. x_proj: rows [0, R) -> Delta_low (R, L); [R, R+N) -> B (N, L); [R+N, R+2N) -> C (N, L)
+  // 3. x_proj: rows [0, R) -> Delta_low, stored token-major (L, R) so that dt_proj contracts over
+  //    its contiguous axis; [R, R+N) -> B (N, L); [R+N, R+2N) -> C (N, L)
   g = GemmArgs{};
   g.A = static_cast<const uint16_t*>(w_x);
   g.lda = E;
@@ -187,24 +190,24 @@ int mamba_block_fwd(const void* hidden, const void* w_in, const float* conv_weig
   g.b_bstride = E * L;
   g.M = R + 2 * N; g.N = L; g.K = E;
   g.ndst = 3;
-  g.dst[0] = {dlow, 0, R, L, R * L, 0};
+  g.dst[0] = {dlow, 0, R, R, R * L, 1};
   g.dst[1] = {bc, R, R + N, L, N * L, 0};
   g.dst[2] = {cc, R + N, R + 2 * N, L, N * L, 0};
   if ((st = gemm_check(g)) != MAMBA_OK) return st;
   if ((st = launch_gemm(g, false, Bt, s)) != MAMBA_OK) return st;
 
-  // 4. dt_proj: Delta_raw (E, L) = W_dt (E x R) * Delta_low
+  // 4. dt_proj: Delta_raw (E, L) = W_dt (E x R) * Delta_low, Delta_low K-contiguous
   g = GemmArgs{};
   g.A = static_cast<const uint16_t*>(w_dt);
   g.lda = R;
   g.B = dlow;
-  g.ldb = L;
+  g.ldb = R;
   g.b_bstride = R * L;
   g.M = E; g.N = L; g.K = R;
   g.ndst = 1;
   g.dst[0] = {dt, 0, E, L, E * L, 0};
   if ((st = gemm_check(g)) != MAMBA_OK) return st;
-  if ((st = launch_gemm(g, false, Bt, s)) != MAMBA_OK) return st;
+  if ((st = launch_gemm(g, true, Bt, s)) != MAMBA_OK) return st;
 
   // 5. selective scan (softplus(Delta_raw + dt_bias), z gate, D skip), bf16 storage
   mamba_dims sd = {Bt, E, N, L, MAMBA_BF16, 0};

@@ -566,10 +566,10 @@ double tile_imbalance(int64_t t) {
 // K step and stage count of the large-tile kernel
 constexpr int kBigBK = 32, kBigStages = 5;
 
-// Whether the large-tile kernel serves this call: B K-contiguous, K a multiple of 64, M at least
-// one tile, and destinations that take 16-byte stores (one orientation for all of them).
+// Whether the large-tile kernel serves this call: B K-contiguous, K a multiple of the K step, M at
+// least one tile, and destinations that take 16-byte stores (one orientation for all of them).
 bool big_ok(const GemmArgs& a, bool b_kcontig) {
-  if (!b_kcontig || a.K % 64 || a.M < 256 || a.N < 128) return false;
+  if (!b_kcontig || a.K % kBigBK || a.M < 256 || a.N < 128) return false;
   for (int i = 0; i < a.ndst; ++i) {
     const GemmDest& d = a.dst[i];
     if (d.trans != a.dst[0].trans) return false;
