@@ -134,7 +134,17 @@ def cpu_baseline(x, w, target_cpu_s):
                 break
         passes += 1
     seqs = done // (w.dim * L)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return dict(value=done / spent, unit="channel-steps/s", cores=cores, kind="oracle",
+                cpu_model=model, usable_cores=len(os.sched_getaffinity(0)),
                 sample=f"{seqs} sequences ({passes} pass(es) over the {w.batch} sequences) x "
                        f"{w.dim} channels x {L} tokens of the {w.name} workload ({done} "
                        f"channel-steps, {spent:.1f} s wall x {cores} threads = "
@@ -497,6 +507,34 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # the same kernel with the last-level cache (MALL, 256 MB) flushed before each launch by a
+    # 512 MB scratch write outside the events: the cold-cache kernel time
+    scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    flushed = []
+    for _ in range(10):
+        scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        flushed.append(a.elapsed_time(b))
+    flushed.sort()
+    # streaming-copy bandwidth of this GPU in the same run (reads 1 GiB, writes 1 GiB)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copies = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        copies.append(a.elapsed_time(b))
+    copy_GBps = 2 * src.numel() * 4 / (sorted(copies)[len(copies) // 2] * 1e-3) / 1e9
+    del scratch, src, dst
+
     alu_achieved = chsteps * ALU_OPS_PER_CHANNEL_STEP / (kern_avg * 1e-3)
     hbm_achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
     traffic = None
@@ -531,10 +569,14 @@ def main():
                      "ops_per_channel_step": ALU_OPS_PER_CHANNEL_STEP},
         "hbm": {"achieved_GBps": hbm_achieved, "peak_GBps": HBM_PEAK_GBS,
                 "frac": hbm_achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg_bytes,
-                "bytes_per_channel_step": alg_bytes / chsteps},
+                "bytes_per_channel_step": alg_bytes / chsteps,
+                "counter_GBps": (traffic / (kern_avg * 1e-3) / 1e9) if traffic else None,
+                "copy_GBps": copy_GBps, "frac_of_copy": hbm_achieved / copy_GBps},
         "kernel_us": {"mean": kern_avg * 1e3, "p10": kern_ms[len(kern_ms) // 10] * 1e3,
                       "median": kern_ms[len(kern_ms) // 2] * 1e3,
                       "p90": kern_ms[(len(kern_ms) * 9) // 10] * 1e3},
+        "kernel_us_mall_flushed": {"median": flushed[len(flushed) // 2] * 1e3,
+                                   "p10": flushed[1] * 1e3, "p90": flushed[-2] * 1e3},
         "outputs_finite": ok,
     }
     if not args.no_conv:
