@@ -11,9 +11,9 @@
 //   1. in_proj   (MFMA GEMM): [x; z] (2E x L per sequence) = W_in (2E x d_model) * hidden^T;
 //                 x and z are written channel-major (E, L), the layout the scan reads.
 //   2. conv      u = silu(causal_conv1d(x) + conv_b) (channel-major, 8 tokens per thread).
-//   3. x_proj    (MFMA GEMM): [Delta_low; B; C] ((R + 2N) x L) = W_x * u; rows are routed to
-//                 three buffers: Delta_low token-major (L, R), B and C in the (N, L) layout of
-//                 the scan.
+//   3. x_proj    (MFMA GEMM, split-K with a deterministic reduction): [Delta_low; B; C]
+//                 ((R + 2N) x L) = W_x * u; rows are routed to three buffers: Delta_low
+//                 token-major (L, R), B and C in the (N, L) layout of the scan.
 //   4. dt_proj   (MFMA GEMM): Delta_raw (E x L) = W_dt (E x R) * Delta_low, both operands
 //                 K-contiguous.
 //   5. scan      y = selective_scan(u, Delta_raw, A, B, C, D, z, dt_bias, softplus); y is stored
@@ -70,10 +70,30 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const uint16_t* __restri
 }
 
 struct BlockLayout {  // workspace regions in bytes, each 256-byte aligned
-  size_t x, z, u, dt, y, dlow, bc, cc, scan, total;
+  size_t x, z, u, dt, y, dlow, bc, cc, part, scan, total;
 };
 
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// x_proj: rows [0, R) -> Delta_low, stored token-major (L, R) so that dt_proj contracts over its
+// contiguous axis; [R, R+N) -> B (N, L); [R+N, R+2N) -> C (N, L).  Long K (d_inner) and only
+// (R + 2N) rows: it runs split-K.
+GemmArgs xproj_args(const mamba_block_dims* d, const void* w_x, const uint16_t* u,
+                    uint16_t* dlow, uint16_t* bc, uint16_t* cc) {
+  const int64_t L = d->seqlen, E = d->d_inner, R = d->dt_rank, N = d->dstate;
+  GemmArgs g = {};
+  g.A = static_cast<const uint16_t*>(w_x);
+  g.lda = E;
+  g.B = u;
+  g.ldb = L;
+  g.b_bstride = E * L;
+  g.M = R + 2 * N; g.N = L; g.K = E;
+  g.ndst = 3;
+  g.dst[0] = {dlow, 0, R, R, R * L, 1};
+  g.dst[1] = {bc, R, R + N, L, N * L, 0};
+  g.dst[2] = {cc, R + N, R + 2 * N, L, N * L, 0};
+  return g;
+}
 
 int block_layout(const mamba_block_dims* d, BlockLayout* o) {
   mamba_dims sd = {d->batch, d->d_inner, d->dstate, d->seqlen, MAMBA_BF16, 0};
@@ -90,6 +110,8 @@ int block_layout(const mamba_block_dims* d, BlockLayout* o) {
   o->dlow = at; at += round256(el * d->dt_rank);
   o->bc = at;   at += round256(el * d->dstate);
   o->cc = at;   at += round256(el * d->dstate);
+  o->part = at; at += round256(gemm_split_bytes(xproj_args(d, nullptr, nullptr, nullptr, nullptr,
+                                                           nullptr), d->batch));
   o->scan = at; at += round256(pl.ws_bytes);
   o->total = at;
   return MAMBA_OK;
@@ -180,21 +202,12 @@ int mamba_block_fwd(const void* hidden, const void* w_in, const float* conv_weig
                      x, conv_weight, conv_bias, u, E, L, dims->conv_width, total8);
   if ((st = launch_status()) != MAMBA_OK) return st;
 
-  // 3. x_proj: rows [0, R) -> Delta_low, stored token-major (L, R) so that dt_proj contracts over
-  //    its contiguous axis; [R, R+N) -> B (N, L); [R+N, R+2N) -> C (N, L)
-  g = GemmArgs{};
-  g.A = static_cast<const uint16_t*>(w_x);
-  g.lda = E;
-  g.B = u;
-  g.ldb = L;
-  g.b_bstride = E * L;
-  g.M = R + 2 * N; g.N = L; g.K = E;
-  g.ndst = 3;
-  g.dst[0] = {dlow, 0, R, R, R * L, 1};
-  g.dst[1] = {bc, R, R + N, L, N * L, 0};
-  g.dst[2] = {cc, R + N, R + 2 * N, L, N * L, 0};
+  // 3. x_proj (split-K into the fp32 partials region, then the routing reduction)
+  g = xproj_args(dims, w_x, u, dlow, bc, cc);
   if ((st = gemm_check(g)) != MAMBA_OK) return st;
-  if ((st = launch_gemm(g, false, Bt, s)) != MAMBA_OK) return st;
+  if ((st = launch_gemm_split(g, false, Bt, reinterpret_cast<float*>(ws + lay.part),
+                              lay.scan - lay.part, s)) != MAMBA_OK)
+    return st;
 
   // 4. dt_proj: Delta_raw (E, L) = W_dt (E x R) * Delta_low, Delta_low K-contiguous
   g = GemmArgs{};

@@ -27,6 +27,12 @@ struct GemmArgs {
   int32_t mtiles, ntiles, ndst;
   int64_t batch;
   GemmDest dst[3];
+  // split-K (register-staged kernel only): workgroup s of ksplit covers K range
+  // [s kchunk, min(K, (s + 1) kchunk)) and writes fp32 partials to part (ksplit, batch, M, N);
+  // ksplit <= 1: one pass, bf16 results straight to the destinations
+  int32_t ksplit;
+  int64_t kchunk;
+  float* part;
 };
 
 // Shape rules the kernels rely on (gemm_check, on the host): M % 16 == 0, N % 8 == 0,
@@ -36,5 +42,14 @@ struct GemmArgs {
 __attribute__((visibility("hidden"))) int gemm_check(const GemmArgs& a);
 __attribute__((visibility("hidden"))) int launch_gemm(const GemmArgs& a, bool b_kcontig,
                                                       int64_t batch, hipStream_t s);
+// Split-K for calls with too few output tiles to fill the GPU (long K, small M x N): the number
+// of splits launch_gemm_split will use, the fp32 workspace it needs, and the launch (the split
+// pass, then a deterministic reduction that sums the splits in order, rounds to bf16 and routes
+// rows to the destinations).  Falls back to launch_gemm when one split is chosen.
+__attribute__((visibility("hidden"))) int gemm_split_factor(const GemmArgs& a, int64_t batch);
+__attribute__((visibility("hidden"))) size_t gemm_split_bytes(const GemmArgs& a, int64_t batch);
+__attribute__((visibility("hidden"))) int launch_gemm_split(const GemmArgs& a, bool b_kcontig,
+                                                            int64_t batch, float* part,
+                                                            size_t part_bytes, hipStream_t s);
 
 }  // namespace mamba

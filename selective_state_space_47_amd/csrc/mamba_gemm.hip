@@ -7,6 +7,7 @@
 // Operand layouts of v_mfma_f32_32x32x16_bf16 on gfx950 (checked with an in-bounds probe): lane l
 // holds A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; accumulator element i of lane
 // l is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+#include <algorithm>
 #include <type_traits>
 
 #include "mamba_gemm.h"
@@ -58,6 +59,7 @@ struct GemmThread {
   GemmSmem<kWM, kWN, kBK>& sm;
   int tid;
   int64_t m0, n0;
+  int64_t kend;  // end of this workgroup's K range (exclusive)
   const uint16_t* Bb;
   uint4 ra[S::PA], rb[4];
 
@@ -71,14 +73,14 @@ struct GemmThread {
       const uint16_t* src = p.A + m * p.lda + k0 + kw;
 #pragma unroll
       for (int j = 0; j < S::PA; ++j)
-        ra[j] = ld16(src + 8 * j, m < p.M && k0 + kw + 8 * j < p.K);
+        ra[j] = ld16(src + 8 * j, m < p.M && k0 + kw + 8 * j < kend);
     }
     if (kBKc) {
       const int r = tid / S::TPRB, kw = (tid % S::TPRB) * 4 * 8;
       const int64_t n = n0 + r;
       const uint16_t* src = Bb + n * p.ldb + k0 + kw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rb[j] = ld16(src + 8 * j, n < p.N && k0 + kw + 8 * j < p.K);
+      for (int j = 0; j < 4; ++j) rb[j] = ld16(src + 8 * j, n < p.N && k0 + kw + 8 * j < kend);
     } else {  // thread -> k rows 4 kg .. 4 kg + 3, columns 8 ng .. 8 ng + 7; consecutive lanes
               // take consecutive k groups, so the 8-byte column pieces they write land in
               // different banks (lanes of equal kg would all hit one bank: 8 rows of 144 bytes
@@ -89,7 +91,7 @@ struct GemmThread {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t k = k0 + 4 * kg + i;
-        rb[i] = ld16(Bb + k * p.ldb + n, k < p.K && n < p.N);
+        rb[i] = ld16(Bb + k * p.ldb + n, k < kend && n < p.N);
       }
     }
   }
@@ -162,11 +164,19 @@ __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(Ge
   const int lane = th.tid & 63;
   const int w = th.tid >> 6;
   const int wm = w >> 1, wn = w & 1;
+  int64_t widx = blockIdx.x, split = 0;
+  if (p.ksplit > 1) {
+    const int64_t tiles = (int64_t)p.mtiles * p.ntiles * p.batch;
+    split = widx / tiles;
+    widx -= split * tiles;
+  }
   int64_t bidx, mt, nt;
-  tile_of(p, blockIdx.x, &bidx, &mt, &nt);
+  tile_of(p, widx, &bidx, &mt, &nt);
   th.m0 = mt * S::TM;
   th.n0 = nt * S::TN;
   th.Bb = p.B + bidx * p.b_bstride;
+  const int64_t kbeg = p.ksplit > 1 ? split * p.kchunk : 0;
+  th.kend = p.ksplit > 1 ? min(p.K, kbeg + p.kchunk) : p.K;
 
   f32x16_t acc[kWM][kWN];
 #pragma unroll
@@ -176,13 +186,13 @@ __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(Ge
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int64_t nk = (p.K + kBK - 1) / kBK;
-  th.load(0);
+  const int64_t nk = (th.kend - kbeg + kBK - 1) / kBK;
+  th.load(kbeg);
   th.store(0);
   __syncthreads();
   for (int64_t ks = 0; ks < nk; ++ks) {
     const int buf = (int)(ks & 1);
-    if (ks + 1 < nk) th.load((ks + 1) * kBK);
+    if (ks + 1 < nk) th.load(kbeg + (ks + 1) * kBK);
     const uint16_t* As = sm.a[buf];
     const uint16_t* Bs = sm.b[buf];
 #pragma unroll
@@ -206,6 +216,24 @@ __global__ __launch_bounds__(256, (kWM * kWN >= 16 ? 1 : 2)) void gemm_kernel(Ge
       th.store(buf ^ 1);  // the other buffer was last read in step ks - 1, before the barrier
       __syncthreads();
     }
+  }
+
+  if (p.ksplit > 1) {  // fp32 partials of this split, (M, N) row-major per batch
+    float* part = p.part + (split * p.batch + bidx) * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+#pragma unroll
+      for (int j = 0; j < kWN; ++j) {
+        const int64_t n = th.n0 + S::TN / 2 * wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t mq = th.m0 + S::TM / 2 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
+          if (mq >= p.M || n >= p.N) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[(mq + r) * p.N + n] = acc[i][j][4 * q + r];
+        }
+      }
+    return;
   }
 
   // ---- epilogue: round to bf16 and route rows to their destination.  The destinations are
@@ -264,6 +292,49 @@ int launch_shape(const GemmArgs& a0, bool b_kcontig, int64_t batch, hipStream_t 
   else
     hipLaunchKernelGGL((gemm_kernel<kWM, kWN, kBK, false>), grid, dim3(256), 0, s, a);
   return launch_status();
+}
+
+// Split-K reduction: thread -> (batch b, 8 rows m8 .. m8+7, column n).  The splits are added in
+// order (deterministic), rounded to bf16 and routed; destinations are visited with constant
+// indices.  A transposed destination takes the 8 rows as one 16-byte store (the host checks
+// ld % 8 == 0 and 16-byte alignment), a row-major one as 8 two-byte stores that consecutive
+// threads (consecutive n) coalesce.
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs p) {
+  const int64_t mg = p.M / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= p.batch * mg * p.N) return;
+  const int64_t n = gid % p.N, r = gid / p.N;
+  const int64_t m8 = (r % mg) * 8, b = r / mg;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int s = 0; s < p.ksplit; ++s) {
+    const float* src = p.part + ((s * p.batch + b) * p.M + m8) * p.N + n;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += src[i * p.N];
+  }
+#pragma unroll
+  for (int di = 0; di < 3; ++di) {
+    if (di >= p.ndst) break;
+    const GemmDest& d = p.dst[di];
+    if (d.ptr == nullptr || m8 < d.m0 || m8 >= d.m1) continue;
+    uint16_t* base = d.ptr + b * d.bstride;
+    const int64_t rr = m8 - d.m0;
+    if (d.trans) {
+      const uint4 w = make_uint4(pack_bf16(make_float2(v[0], v[1])),
+                                 pack_bf16(make_float2(v[2], v[3])),
+                                 pack_bf16(make_float2(v[4], v[5])),
+                                 pack_bf16(make_float2(v[6], v[7])));
+      *reinterpret_cast<uint4*>(base + n * d.ld + rr) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const uint32_t w = pack_bf16(make_float2(v[i], v[i + 1]));
+        base[(rr + i) * d.ld + n] = (uint16_t)(w & 0xffffu);
+        base[(rr + i + 1) * d.ld + n] = (uint16_t)(w >> 16);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ large-tile kernel
@@ -629,6 +700,53 @@ int launch_gemm(const GemmArgs& a, bool b_kcontig, int64_t batch, hipStream_t s)
     return launch_big<128, kBigBK, kBigStages>(a, batch, s);
   }
   return launch_shape<2, 2, 64>(a, b_kcontig, batch, s);
+}
+
+int gemm_split_factor(const GemmArgs& a, int64_t batch) {
+  // enough workgroups for about four per CU of the register-staged kernel, each with a K range
+  // of at least 512; the reduction stores 8 rows of a transposed destination as one 16-byte word
+  const int64_t tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128) * batch;
+  int64_t ks = tiles > 0 ? 1024 / tiles : 1;
+  ks = std::min<int64_t>(ks, a.K / 512);
+  ks = std::min<int64_t>(ks, 8);
+  if (ks < 2 || a.M % 8) return 1;
+  for (int i = 0; i < a.ndst; ++i)
+    if (a.dst[i].ptr && a.dst[i].trans && (a.dst[i].ld % 8 || !aligned(a.dst[i].ptr, 16)))
+      return 1;
+  return (int)ks;
+}
+
+size_t gemm_split_bytes(const GemmArgs& a, int64_t batch) {
+  const int ks = gemm_split_factor(a, batch);
+  return ks > 1 ? (size_t)ks * batch * a.M * a.N * sizeof(float) : 0;
+}
+
+int launch_gemm_split(const GemmArgs& a0, bool b_kcontig, int64_t batch, float* part,
+                      size_t part_bytes, hipStream_t s) {
+  const int ks = gemm_split_factor(a0, batch);
+  if (ks < 2 || big_ok(a0, b_kcontig)) return launch_gemm(a0, b_kcontig, batch, s);
+  if (!part || part_bytes < gemm_split_bytes(a0, batch)) return MAMBA_ERR_WORKSPACE;
+  using S = TileShape<2, 2, 64>;
+  GemmArgs a = a0;
+  a.mtiles = (int32_t)((a.M + S::TM - 1) / S::TM);
+  a.ntiles = (int32_t)((a.N + S::TN - 1) / S::TN);
+  a.batch = batch;
+  a.ksplit = ks;
+  a.kchunk = ((a.K + ks - 1) / ks + 63) / 64 * 64;
+  a.part = part;
+  const int64_t tiles = (int64_t)a.mtiles * a.ntiles * batch;
+  if (tiles * ks > 0x7fffffffLL) return MAMBA_ERR_SHAPE;
+  const dim3 grid((unsigned)(tiles * ks));
+  if (b_kcontig)
+    hipLaunchKernelGGL((gemm_kernel<2, 2, 64, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<2, 2, 64, false>), grid, dim3(256), 0, s, a);
+  int st = launch_status();
+  if (st != MAMBA_OK) return st;
+  const int64_t threads = batch * (a.M / 8) * a.N;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, a);
+  return launch_status();
 }
 
 }  // namespace mamba

@@ -44,9 +44,14 @@ def run(p):
 
 @pytest.mark.parametrize("shape", [(1, 8, 16, 16, 16, 1), (2, 64, 32, 48, 16, 4),
                                    (2, 136, 64, 128, 16, 4), (1, 256, 256, 512, 32, 3),
-                                   (3, 40, 144, 272, 48, 2)],
+                                   (3, 40, 144, 272, 48, 2), (1, 128, 64, 1024, 32, 4)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_block_small(shape):
+    """(batch, L, d_model, d_inner, dt_rank, conv width).  (1, 256, 256, 512, 32, 3) runs in_proj,
+    dt_proj and out_proj on the large-tile GEMM (in_proj with two destinations);
+    (3, 40, 144, 272, 48, 2) takes the register-staged kernel for all of them, with a ragged token
+    count and a partial channel block in the scan; (1, 128, 64, 1024, 32, 4) runs x_proj split-K
+    (K = 1024 over one output tile: two splits)."""
     batch, L, d_model, E, R, W = shape
     p = synth.block_inputs(synth.BlockWorkload("t", batch, L, d_model, E, R, W, 31 + L))
     print(f"[block] batch={batch} L={L} d_model={d_model} E={E} R={R} W={W}", flush=True)
