@@ -221,7 +221,8 @@ typedef struct mamba_block_dims {
 } mamba_block_dims;
 
 /* Bytes of device workspace mamba_block_fwd needs (0 for invalid dims): the bf16 intermediates
- * x, z, u, Delta_raw, y (5 x batch*E*L), Delta_low, B, C and the scan's chunk records. */
+ * x, z, u, Delta_raw, y (5 x batch*E*L), Delta_low, B, C, the fp32 split-K partials of the
+ * W_x projection (when it is split) and the scan's chunk records. */
 size_t mamba_block_workspace_bytes(const mamba_block_dims* dims);
 
 /*
