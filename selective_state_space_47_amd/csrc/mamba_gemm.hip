@@ -151,8 +151,10 @@ __device__ __forceinline__ void tile_of(const GemmArgs& p, int64_t w, int64_t* b
 // Register-staged kernel.  Workgroup tile 128 x 128, K step 64, 256 threads = 4 waves in a 2 x 2
 // grid, each wave 2 x 2 MFMA tiles (fp32 accumulators, 64 registers).  Both operand tiles live in
 // LDS with K contiguous, rows padded by 16 bytes (pitch 144 bytes: the 16-byte fragment reads of
-// 8 consecutive rows hit all 32 banks of a 128-byte cycle), double buffered: the next K step is
-// loaded into registers while the current one is multiplied.  An N-contiguous B tile is
+// 16 consecutive rows, one pass of the 64-bank LDS, land at 16 different 16-byte positions of a
+// 256-byte bank cycle), double buffered: the next K step is loaded into registers while the
+// current one is multiplied.  With ksplit > 1 a workgroup covers one K range and writes fp32
+// partials instead (split-K, reduced by split_reduce_kernel).  An N-contiguous B tile is
 // transposed in registers on its way to LDS (4 k-rows x 8 columns per thread, packed into 8-byte
 // column pieces).
 template <int kWM, int kWN, int kBK, bool kBKc>

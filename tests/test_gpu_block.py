@@ -77,3 +77,13 @@ def test_block_2p8b_first_tokens():
     e = rel_err(out[:, :64], ref)
     print(f"[block_2p8b] first 64 tokens rel err {e:.2e}", flush=True)
     assert e <= 2e-2
+
+
+def test_block_deterministic():
+    """Two calls on the same inputs agree bit for bit (the split-K reduction of x_proj adds its
+    partials in a fixed order; nothing else reduces across workgroups)."""
+    p = synth.block_inputs(synth.BlockWorkload("t", 2, 128, 64, 1024, 32, 4, 77))
+    print("[block determinism] batch=2 L=128 d_model=64 E=1024 R=32 W=4", flush=True)
+    a = run(p)
+    b = run(p)
+    assert np.array_equal(a, b)
