@@ -404,7 +404,8 @@ template <int kN>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
 }
-// wait_vm<c * kD> for a count c in [0, kMax] known only at run time (uniform)
+// wait_vm<c * kD> for a count c in [0, kMax] known only at run time (uniform); a count above 4
+// waits for 4 kD, which is more conservative than needed and still correct
 template <int kD, int kMax>
 __device__ __forceinline__ void wait_vm_steps(int c) {
   if (kMax >= 4 && c >= 4) { wait_vm<(kMax >= 4 ? 4 * kD : 0)>(); return; }

@@ -52,6 +52,8 @@ struct __align__(16) ScanSmem {
 // kMode = kModeSummary: chunk summary (local final state from zero and sum of Delta), no output.
 // kMode = kModeCkpt: carry-in and recurrence only; the state before every 8th token is stored
 //   (the backward pass recomputes each 8-token block from these checkpoints).
+// kMode = kModeMainT: as kModeMain with out stored token-major, (batch, L, dim) (bf16, vector
+//   I/O, dim % 8 == 0; the layout the block's output projection contracts over).
 // kVec: seqlen % 8 == 0 and 16-byte aligned tensors -> vector loads and stores.
 // kSoftplus / kGate: softplus on Delta / z gate present (compile-time, no per-element selects).
 // kConv: the loaded input is x and u = silu(causal depthwise conv1d(x) + bias) is formed in the

@@ -39,12 +39,13 @@ def bf16(rng, shape, scale=1.0):
 # (256, 128, 64, 1) one 256 x 256 tile half outside N and a single K step; (272, 136, 128, 2) and
 # (1040, 520, 192, 3) ragged M and N on 256 x 128 tiles, the latter with an odd number of K
 # steps; (4096, 2048, 512, 4) 256 x 256 tiles; (512, 256, 160, 2) and (272, 136, 96, 1) K a
-# multiple of the 32-deep K step but not of 64, with fewer K steps than stages (5 and 3).
+# multiple of the 32-deep K step but not of 64, with fewer K steps than stages (5 and 3);
+# (256, 256, 32, 2) a single K step (the load prologue only).
 SHAPES = [(16, 8, 8, 1), (128, 128, 64, 1), (144, 200, 136, 2), (256, 384, 520, 3),
           (192, 264, 5120, 2), (5120, 136, 160, 1), (48, 1000, 72, 2),
           (4096, 2048, 512, 4), (4112, 2056, 520, 4),
           (256, 128, 64, 1), (272, 136, 128, 2), (1040, 520, 192, 3),
-          (512, 256, 160, 2), (272, 136, 96, 1)]
+          (512, 256, 160, 2), (272, 136, 96, 1), (256, 256, 32, 2)]
 
 
 @pytest.mark.parametrize("b_kcontig", [True, False])
