@@ -644,6 +644,8 @@ constexpr int kBigBK = 32, kBigStages = 5;
 // least one tile, and destinations that take 16-byte stores (one orientation for all of them).
 bool big_ok(const GemmArgs& a, bool b_kcontig) {
   if (!b_kcontig || a.K % kBigBK || a.M < 256 || a.N < 128) return false;
+  // the per-lane load offsets within a tile are 32-bit: 256 rows of either operand
+  if (256 * a.lda * 2 >= ((int64_t)1 << 32) || 256 * a.ldb * 2 >= ((int64_t)1 << 32)) return false;
   for (int i = 0; i < a.ndst; ++i) {
     const GemmDest& d = a.dst[i];
     if (d.trans != a.dst[0].trans) return false;
