@@ -7,9 +7,9 @@ seeded synthetic data resident in HBM before timing starts.  The single-token st
 the generation workload (256 x 5120 x 16 fp32 states, bf16 tokens) is timed in the same run and
 reported in its own field.
 
-Prints one JSON line.  Roofline: the scan is bound by VALU issue on gfx950 (see the design doc for
-the derivation of the per-channel-step op count and the peak); the HBM figure the metric names
-is reported next to it.
+Prints one JSON line.  Roofline: the scan is bound by VALU issue on gfx950 (ALU_PEAK_LANE_OPS and
+ALU_OPS_PER_CHANNEL_STEP below give the peak and the per-channel-step op count); the HBM figure
+the metric names is reported next to it.
 """
 from __future__ import annotations
 
@@ -439,8 +439,8 @@ def main():
         parse_counters(args.parse_counters[0], args.parse_counters[1], PROFILE_COUNTERS, alg_bytes)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the selective scan on a single "
-              "MI355X (channels are independent; see DESIGN.md for how the path would shard). "
+        print("bench.py measures one GPU only: the selective scan runs on a single MI355X here "
+              "(channels are independent, so the path would shard over batch or channels). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 

@@ -44,7 +44,7 @@ class Workload:
     bias_hi: float
     seed: int
     steps: int = 0         # >0: generation-step workload (state update repeated `steps` times)
-    tol: float = 1e-4      # parity bound, see the design doc
+    tol: float = 1e-4      # parity bound of the GPU tests for this workload
     tol_kind: str = "rel"  # "rel": max|err|/max(|ref|, rms(ref)); "rms": max|err|/rms(ref)
 
     @property
