@@ -127,11 +127,18 @@ int check_block(const mamba_block_dims* d) {
   if (d->seqlen % 8 || d->d_model % 16 || d->d_inner % 16 || d->dt_rank % 16)
     return MAMBA_ERR_SHAPE;
   if (d->batch > 65535) return MAMBA_ERR_SHAPE;
+  // every GEMM dimension stays below 2^31 (the projections' tile counts are 32-bit)
+  const int64_t dlim = (int64_t)1 << 30;
+  if (d->seqlen > dlim || d->d_model > dlim || d->d_inner > dlim || d->dt_rank > dlim)
+    return MAMBA_ERR_SHAPE;
   const double lim = (double)((int64_t)1 << 40);
-  if ((double)d->batch * (double)d->seqlen * (double)(2 * d->d_inner) > lim ||
+  if ((double)d->batch * (double)d->seqlen * 2.0 * (double)d->d_inner > lim ||
       (double)d->batch * (double)d->seqlen * (double)d->d_model > lim)
     return MAMBA_ERR_SHAPE;
-  return MAMBA_OK;
+  // the scan's own limits (token count against its 32-bit row offsets), checked before anything
+  // is launched
+  const mamba_dims sd = {d->batch, d->d_inner, d->dstate, d->seqlen, MAMBA_BF16, 0};
+  return check_dims(&sd, false);
 }
 
 }  // namespace

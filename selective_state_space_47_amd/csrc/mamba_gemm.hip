@@ -678,11 +678,17 @@ int gemm_check(const GemmArgs& a) {
   if (!a.A || !a.B) return MAMBA_ERR_NULL;
   if (a.M <= 0 || a.N <= 0 || a.K <= 0 || a.M % 16 || a.N % 8 || a.K % 8) return MAMBA_ERR_SHAPE;
   if (a.lda < a.K || a.lda % 8 || a.ldb % 8 || a.ldb <= 0) return MAMBA_ERR_SHAPE;
+  // sizes and leading dimensions below 2^31 (tile counts are 32-bit), batch strides below 2^40
+  const int64_t lim = (int64_t)1 << 31, slim = (int64_t)1 << 40;
+  if (a.M >= lim || a.N >= lim || a.K >= lim || a.lda >= lim || a.ldb >= lim ||
+      a.b_bstride < 0 || a.b_bstride >= slim)
+    return MAMBA_ERR_SHAPE;
   if (!aligned(a.A, 16) || !aligned(a.B, 16)) return MAMBA_ERR_ALIGN;
   if (a.ndst < 1 || a.ndst > 3) return MAMBA_ERR_SHAPE;
   for (int i = 0; i < a.ndst; ++i) {
     const GemmDest& d = a.dst[i];
     if (d.m0 % 16 || d.m1 % 16 || d.m0 < 0 || d.m1 <= d.m0 || d.m1 > a.M) return MAMBA_ERR_SHAPE;
+    if (d.ld < 0 || d.ld >= lim || d.bstride < 0 || d.bstride >= slim) return MAMBA_ERR_SHAPE;
     if (i > 0 && d.m0 != a.dst[i - 1].m1) return MAMBA_ERR_SHAPE;
     if (d.ptr && d.trans && (d.ld % 4 || !aligned(d.ptr, 8))) return MAMBA_ERR_ALIGN;
     if (d.ptr && !aligned(d.ptr, 2)) return MAMBA_ERR_ALIGN;

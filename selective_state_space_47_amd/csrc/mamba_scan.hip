@@ -568,13 +568,13 @@ int scan_forward(const void* u, const float* conv_w, const float* conv_b, int co
   const bool vec = dims->seqlen % 8 == 0 && aligned(u, 16) && aligned(delta, 16) &&
                    aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16)) &&
                    (!a.u_out || aligned(a.u_out, 16));
+  if (out_tmajor && (conv_w || !bf || !vec || dims->dim % 8 || !aligned(out, 16)))
+    return MAMBA_ERR_UNSUPPORTED;
   if (pl.nchunks > 1) {
     dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
     if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
       return MAMBA_ERR_HIP;
   }
-  if (out_tmajor && (conv_w || !bf || !vec || dims->dim % 8 || !aligned(out, 16)))
-    return MAMBA_ERR_UNSUPPORTED;
   dim3 grid((unsigned)(nwg_ch * pl.nchunks));
   return launch_fwd(out_tmajor ? kModeMainT : kModeMain, bf, vec, softplus_flag != 0,
                     z != nullptr, grid, s, a);

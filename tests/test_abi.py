@@ -158,3 +158,58 @@ def test_conv_validation_codes(lib):
     assert conv(dm, x=None) == -1
     assert conv(dm, u_out=ODD) == -5
     assert conv(dims(batch=1, dim=64, seqlen=128, chunk=8)) == -2
+
+
+def bdims(batch=1, L=128, dm=64, E=128, R=16, width=4, dstate=16):
+    return binding.mamba_block_dims(batch, L, dm, E, dstate, R, width, 0)
+
+
+def call_block(lib, bd, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.mamba_block_workspace_bytes(ctypes.byref(bd)) if bd is not None else 0
+    return lib.mamba_block_fwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
+                               ctypes.byref(bd) if bd is not None else None, ws, ws_bytes, None)
+
+
+def test_block_validation_codes(lib):
+    assert call_block(lib, None) == -1
+    assert call_block(lib, bdims(), ws=None) == -6
+    need = lib.mamba_block_workspace_bytes(ctypes.byref(bdims()))
+    assert need > 0
+    assert call_block(lib, bdims(), ws_bytes=need - 1) == -6
+    assert call_block(lib, bdims(), ws=ctypes.c_void_p(0x10010)) == -5   # workspace needs 256-B
+    assert call_block(lib, bdims(dstate=8)) == -4
+    assert call_block(lib, bdims(width=5)) == -4
+    assert call_block(lib, bdims(L=124)) == -2                            # tokens % 8
+    assert call_block(lib, bdims(E=120)) == -2                            # d_inner % 16
+    assert call_block(lib, bdims(batch=65536)) == -2
+    # the scan's token bound (2^26 bf16 tokens) is enforced before the first projection runs
+    big = bdims(L=1 << 26, dm=16, E=16)
+    assert lib.mamba_block_workspace_bytes(ctypes.byref(big)) == 0
+    assert call_block(lib, big, ws_bytes=1 << 40) == -2
+    for v in (2 ** 63 - 1, 2 ** 40, -1):
+        for f in ("batch", "seqlen", "d_model", "d_inner", "dt_rank"):
+            bd = bdims()
+            setattr(bd, f, v - (v % 16 if v > 0 else 0))
+            assert lib.mamba_block_workspace_bytes(ctypes.byref(bd)) == 0
+            assert call_block(lib, bd, ws_bytes=2 ** 63) == -2, (f, v)
+
+
+def test_gemm_validation_codes(lib):
+    def gemm(M=256, N=128, K=64, batch=1, lda=64, ldb=64, bs=0, ldc=128, cs=0, kc=1, tr=0,
+             A=FAKE):
+        return lib.mamba_gemm_bf16(A, FAKE, FAKE, M, N, K, batch, lda, ldb, bs, ldc, cs, kc, tr,
+                                   None)
+    assert gemm(A=None) == -1
+    assert gemm(A=ODD) == -5
+    assert gemm(M=250) == -2 and gemm(N=100) == -2 and gemm(K=60, lda=64) == -2
+    assert gemm(batch=0) == -2 and gemm(batch=65536) == -2
+    assert gemm(ldb=32) == -2                      # K-contiguous B needs ldb >= K
+    assert gemm(ldc=100) == -2                     # row-major C needs ldc >= N
+    assert gemm(tr=1, ldc=254) == -5               # transposed C needs ldc % 4 == 0
+    # sizes at or past 2^31 (32-bit tile counts) and strides past 2^40 elements
+    big = 2 ** 63 - 16
+    assert gemm(M=big) == -2 and gemm(N=big) == -2 and gemm(M=2 ** 31, lda=64) == -2
+    assert gemm(K=2 ** 31, lda=2 ** 31, ldb=2 ** 31) == -2
+    assert gemm(bs=2 ** 40) == -2 and gemm(bs=-8) == -2 and gemm(cs=2 ** 40) == -2
+    assert gemm(ldc=2 ** 31) == -2

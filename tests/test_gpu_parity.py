@@ -339,6 +339,42 @@ def test_prefill_then_decode_equals_scan():
     assert rel_err(state.cpu().numpy(), rl) <= 1e-4
 
 
+def test_linear_in_u_without_gate():
+    """With the gate off and Delta, B, C fixed, y and the final state are linear in u (the
+    recurrence is a linear time-varying system in its input)."""
+    x = synth.random_case(46, 2, 40, 200)
+    rng = np.random.default_rng(46)
+    u2 = rng.standard_normal(x["u"].shape).astype(np.float32)
+    a, b = 0.75, -1.25
+    y1, l1 = gpu_scan(x, torch.float32, use_z=False)
+    y2, l2 = gpu_scan(dict(x, u=u2), torch.float32, use_z=False)
+    y3, l3 = gpu_scan(dict(x, u=(a * x["u"] + b * u2).astype(np.float32)), torch.float32,
+                      use_z=False)
+    assert rel_err(y3, a * y1.astype(np.float64) + b * y2, "rms") <= 1e-5
+    assert rel_err(l3, a * l1.astype(np.float64) + b * l2, "rms") <= 1e-5
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_channel_and_batch_permutation_equivariance(io):
+    """Channels and sequences are independent: permuting them permutes the outputs exactly.
+    dim = 70 puts channels in different lanes, workgroups and the ragged tail."""
+    x = synth.random_case(47, 3, 70, 150, bf16=io == torch.bfloat16)
+    rng = np.random.default_rng(47)
+    pc, pb = rng.permutation(70), rng.permutation(3)
+    xp = {}
+    for k, v in x.items():
+        if k in ("u", "delta", "z"):
+            v = v[pb][:, pc]
+        elif k in ("B", "C"):
+            v = v[pb]
+        else:                                   # A, D, delta_bias: per channel
+            v = v[pc]
+        xp[k] = np.ascontiguousarray(v)
+    y, last = gpu_scan(x, io, chunk_len=64)
+    yp, lastp = gpu_scan(xp, io, chunk_len=64)
+    assert np.array_equal(yp, y[pb][:, pc]) and np.array_equal(lastp, last[pb][:, pc])
+
+
 def test_nan_poisons_only_its_channel_from_that_token():
     x = synth.random_case(43, 1, 16, 100)
     x["u"][0, 5, 37] = np.nan

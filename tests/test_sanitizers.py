@@ -1,0 +1,100 @@
+"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
+
+Two programs are built and run:
+  * ``sanitize/oracle_checks.c`` with the fp64 oracle (gcc), calling every oracle function on
+    exact-size buffers, degenerate shapes and every combination of absent optional inputs;
+  * ``sanitize/abi_checks.c`` with the library's sources (hipcc, sanitizers on the host pass
+    only), driving every C entry point through validation and the workspace queries, with sizes
+    up to the int64 limits.  Nothing there passes validation, so nothing is launched.
+A planted out-of-bounds read checks that the sanitizer runtime is live in this toolchain.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SAN = os.path.join(HERE, "sanitize")
+ORACLE_C = os.path.join(ROOT, "oracle", "mamba_oracle.c")
+CSRC = os.path.join(ROOT, "selective_state_space_47_amd", "csrc")
+HIP_SOURCES = ["mamba_scan.hip", "mamba_scan_bwd.hip", "mamba_gemm.hip", "mamba_block.hip"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+CLANG = os.path.join(ROCM, "llvm", "bin", "clang")
+
+GCC_SAN = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all"]
+# sanitizers on the host pass only; the device pass is the ordinary gfx950 build
+HIP_SAN = ["--offload-arch=gfx950", "-O1", "-std=c++17", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument"]
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+           UBSAN_OPTIONS="print_stacktrace=1")
+
+
+def _run(cmd, env=None, cwd=None):
+    return subprocess.run(cmd, capture_output=True, text=True, env=env, cwd=cwd, timeout=600)
+
+
+def _need(path):
+    if not (shutil.which(path) or os.path.exists(path)):
+        pytest.skip(f"{path} not available")
+
+
+def test_sanitizer_catches_a_planted_overread(tmp_path):
+    _need("gcc")
+    src = tmp_path / "planted.c"
+    src.write_text("#include <stdlib.h>\nint main(void) { volatile double* p = malloc(4 * "
+                   "sizeof(double)); double s = 0; for (int i = 0; i <= 4; ++i) s += p[i]; "
+                   "free((void*)p); return s > 1e300; }\n")
+    exe = str(tmp_path / "planted")
+    r = _run(["gcc"] + GCC_SAN + ["-o", exe, str(src)])
+    assert r.returncode == 0, r.stderr
+    r = _run([exe], env=ENV)
+    # UBSan's object-size check or ASan's heap redzone, whichever sees it first
+    assert r.returncode != 0
+    assert "heap-buffer-overflow" in r.stderr or "insufficient space" in r.stderr, r.stderr
+
+
+def test_oracle_under_asan_ubsan(tmp_path):
+    _need("gcc")
+    exe = str(tmp_path / "oracle_checks")
+    r = _run(["gcc"] + GCC_SAN + ["-std=c11", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+                                  "-o", exe, os.path.join(SAN, "oracle_checks.c"), ORACLE_C,
+                                  "-lm"])
+    assert r.returncode == 0, r.stderr
+    r = _run([exe], env=ENV)
+    assert r.returncode == 0 and "clean" in r.stdout, r.stdout + r.stderr
+
+
+def test_c_abi_host_code_under_asan_ubsan(tmp_path):
+    _need(HIPCC)
+    _need(CLANG)
+    procs = []
+    for f in HIP_SOURCES:
+        obj = str(tmp_path / (f + ".o"))
+        cmd = [HIPCC] + HIP_SAN + ["-I", os.path.join(ROOT, "include"), "-c",
+                                   os.path.join(CSRC, f), "-o", obj]
+        procs.append((obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                            stderr=subprocess.PIPE, text=True)))
+    objs = []
+    for obj, p in procs:
+        _, err = p.communicate(timeout=600)
+        assert p.returncode == 0, err
+        objs.append(obj)
+    drv = str(tmp_path / "abi_checks.o")
+    r = _run([CLANG, "-O1", "-g", "-std=c11", "-fno-omit-frame-pointer",
+              "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-I",
+              os.path.join(ROOT, "include"), "-c", os.path.join(SAN, "abi_checks.c"), "-o", drv])
+    assert r.returncode == 0, r.stderr
+    exe = str(tmp_path / "abi_checks")
+    r = _run([HIPCC, "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-o", exe,
+              drv] + objs)
+    assert r.returncode == 0, r.stderr
+    # the HIP runtime keeps allocations until exit; leak reports would be its own
+    r = _run([exe], env=dict(ENV, ASAN_OPTIONS="detect_leaks=0"))
+    assert r.returncode == 0 and "clean" in r.stdout, r.stdout + r.stderr
