@@ -276,6 +276,22 @@ inline int make_plan(const mamba_dims* dm, Plan* pl) {
   return MAMBA_OK;
 }
 
+// Workgroup placement on this GPU (measured): workgroup id goes to XCD id % 8, and within an
+// XCD the workgroup with local index l = id / 8 runs on CU l % kCUsPerXCD; when the whole grid is
+// resident, a CU's workgroups are l, l + kCUsPerXCD, l + 2*kCUsPerXCD, ...
+constexpr uint32_t kCUsPerXCD = 32;
+
+// Bijection of [0, n) onto itself that gives every XCD a contiguous range of indices and, inside
+// it, every CU a contiguous sub-range, so that workgroups sharing a CU take neighbouring indices.
+// Under any other placement it is still a bijection; only the locality is lost.
+__host__ __device__ __forceinline__ int64_t placed_index(uint32_t id, uint32_t n) {
+  const uint32_t q = n >> 3, r = n & 7, x = id & 7, l = id >> 3;
+  const uint32_t nx = q + (x < r ? 1u : 0u);  // workgroups on this XCD
+  const uint32_t full = nx / kCUsPerXCD, rem = nx % kCUsPerXCD;
+  const uint32_t c = l % kCUsPerXCD, m = l / kCUsPerXCD;
+  return (int64_t)(x * q + (x < r ? x : r) + c * full + (c < rem ? c : rem) + m);
+}
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }

@@ -274,9 +274,16 @@ __global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
   th.g = th.lane & 7;
   const int g = th.g;
 
+  // Workgroup -> (channel block, chunk) in channel-block-major order, placed so that an XCD
+  // takes a contiguous range of channel blocks and the workgroups sharing a CU take neighbouring
+  // chunks of the same 32 rows.  A workgroup streams 32 rows of 4 tensors; in long sequences
+  // rows lie megabytes apart, and five unrelated workgroups per CU overflow its address-
+  // translation cache.
   const int64_t nwg_ch = (int64_t)p.batch * p.dblocks;
-  const int64_t k = blockIdx.x / nwg_ch;          // chunk
-  const int64_t cb = blockIdx.x - k * nwg_ch;     // channel block
+  const int64_t nk = (int64_t)gridDim.x / nwg_ch;  // chunks in this launch
+  const int64_t j = placed_index(blockIdx.x, gridDim.x);
+  const int64_t cb = j / nk;                       // channel block
+  const int64_t k = j - cb * nk;                   // chunk
   const int64_t b = cb / p.dblocks;
   const int64_t d = (cb - b * p.dblocks) * kChWG + th.w * kChW + th.c;
   // lanes of channels >= dim read a valid row (the block's first channel) and never store

@@ -95,9 +95,13 @@ __global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, c = lane >> 3, g = lane & 7;
+  // (channel block, chunk) in channel-block-major order with the forward's placement: an XCD
+  // takes a contiguous range of channel blocks, a CU neighbouring chunks of the same rows
   const int64_t nwg_ch = p.batch * p.dblocks;
-  const int64_t kq = blockIdx.x / nwg_ch;
-  const int64_t cb = blockIdx.x - kq * nwg_ch;
+  const int64_t nk = (int64_t)gridDim.x / nwg_ch;
+  const int64_t jw = placed_index(blockIdx.x, gridDim.x);
+  const int64_t cb = jw / nk;
+  const int64_t kq = jw - cb * nk;
   const int64_t k = kq + (kSum ? 1 : 0);  // chunk (the summary pass skips chunk 0)
   const int64_t b = cb / p.dblocks;
   const int64_t blk = cb - b * p.dblocks;

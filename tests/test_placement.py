@@ -1,0 +1,24 @@
+"""The workgroup placement map of the scan kernels (host build of the header function, CPU)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
+def test_placement_map_is_a_contiguous_bijection(tmp_path):
+    if not (shutil.which(HIPCC) or os.path.exists(HIPCC)):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "placement_check")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17",
+                        "-I", os.path.join(ROOT, "include"),
+                        "-I", os.path.join(ROOT, "selective_state_space_47_amd", "csrc"),
+                        "-o", exe, os.path.join(HERE, "host", "placement_check.hip")],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "bijective" in r.stdout, r.stdout + r.stderr
