@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mamba_scan.h"
 
 namespace mamba {
@@ -21,7 +23,15 @@ constexpr int kYStride = 18;           // floats per lane slot of the partial-re
 constexpr int kChunkAlign = 16;        // chunk lengths are multiples of this
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTargetWG = 1280;        // 5 workgroups of 4 waves per CU on 256 CUs
+// Automatic chunking (measured on the 256-CU part): sequences are split only when their channel
+// blocks give fewer than kFillWG workgroups (3 per CU); then into enough chunks of at least
+// kMinFillChunk tokens to reach kFillWG, and, for long sequences, into more chunks of at least
+// kMinLongChunk tokens, up to about kLongWG workgroups: several waves of short workgroups
+// finish more evenly than one wave of long ones (9% at 2^20 tokens of 1536 channels).
+constexpr int64_t kFillWG = 768;
+constexpr int64_t kMinFillChunk = 64;
+constexpr int64_t kLongWG = 6144;
+constexpr int64_t kMinLongChunk = 2048;
 
 // ------------------------------------------------------------------ element access
 //
@@ -258,12 +268,13 @@ inline int make_plan(const mamba_dims* dm, Plan* pl) {
   const int64_t nwg_ch = dm->batch * pl->dblocks;
   int64_t cl = dm->chunk_len;
   if (cl == 0) {
-    // as many chunks as keep every workgroup of the main pass resident at once (5 per CU on
-    // 256 CUs): a second round of a few workgroups would nearly double a long pass
-    int64_t K = kTargetWG / nwg_ch;
-    const int64_t maxK = (L + kChunkAlign - 1) / kChunkAlign;
-    if (K > maxK) K = maxK;
-    if (K < 1) K = 1;
+    int64_t K = 1;
+    const int64_t fill = (kFillWG + nwg_ch - 1) / nwg_ch;
+    if (fill > 1) {
+      K = std::min(fill, (L + kMinFillChunk - 1) / kMinFillChunk);
+      const int64_t K_long = std::min(L / kMinLongChunk, (kLongWG + nwg_ch - 1) / nwg_ch);
+      K = std::max(K, K_long);
+    }
     cl = ((L + K - 1) / K + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
   }
   pl->chunk_len = cl;

@@ -94,6 +94,23 @@ def test_workspace_bytes(lib):
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(dims(batch=0))) == 0
 
 
+def test_automatic_chunk_plan(lib):
+    """Chunks only when the channel blocks alone give fewer than 768 workgroups; then enough
+    chunks of >= 64 tokens to reach 768, and for long sequences chunks of >= 2048 tokens up to
+    about 6144 workgroups.  The plan shows in the workspace: 17 floats per channel and chunk but
+    the last."""
+    def ws(batch, dim, L):
+        return lib.mamba_scan_workspace_bytes(ctypes.byref(dims(batch=batch, dim=dim, seqlen=L)))
+    rec = lambda nch, K: nch * (K - 1) * 17 * 4
+    assert ws(8, 5120, 4096) == 0                 # 1280 channel blocks: never chunked
+    assert ws(6, 5120, 1 << 16) == 0              # 960 channel blocks
+    assert ws(2, 1536, 2048) == rec(3072, 8)      # 96 blocks: 8 chunks of 256 (fill)
+    assert ws(1, 1536, 1 << 17) == rec(1536, 64)  # 48 blocks: 64 chunks of 2048 (long)
+    assert ws(1, 1536, 1 << 20) == rec(1536, 128)  # 128 chunks of 8192: 6144 workgroups
+    assert ws(1, 64, 256) == rec(64, 4)           # 2 blocks, short: 4 chunks of 64
+    assert ws(1, 64, 100) == rec(64, 2)           # chunk 50 rounds up to 64: 2 chunks
+
+
 def test_step_validation_codes(lib):
     def step(dm, state=FAKE, u=FAKE, out=FAKE):
         return lib.mamba_state_update(state, u, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, out,
@@ -133,11 +150,12 @@ def test_bwd_validation_codes(lib):
 
 
 def test_bwd_workspace_bytes(lib):
-    # (batch 2, dim 64, L 128) -> 4 workgroups per chunk, chunks of 16 tokens (K = 8):
+    # (batch 2, dim 64, L 128) -> 4 workgroups per chunk; the automatic plan fills the GPU with
+    # chunks of at least 64 tokens: K = 2 chunks of 64
     # forward and adjoint chunk records, checkpoints, per-workgroup dB/dC sums, dA/dD/dbias
     # partials, each region rounded up to 64 floats
     r = lambda n: (n + 63) // 64 * 64
-    nch, K, L = 2 * 64, 8, 128
+    nch, K, L = 2 * 64, 2, 128
     want = (r(nch * (K - 1) * 17) * 2 + r(nch * (L // 8) * 16) + r(2 * 2 * L * 32) +
             r(2 * K * 64 * 16) + 2 * r(2 * K * 64)) * 4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(dims())) == want

@@ -100,15 +100,15 @@ FLAGS = [dict(softplus=s, use_D=d, use_z=z, use_bias=b)
 @pytest.mark.parametrize("flags", FLAGS, ids=lambda f: "".join(
     k[4 if k.startswith("use_") else 0] if v else "-" for k, v in f.items()))
 def test_bwd_flags_small(flags):
-    """Every flag combination; dim 40 (a partial channel block), L 100 (a partial 8-token block,
-    chunked automatically into 7 chunks of 16)."""
+    """Every flag combination; dim 40 (a partial channel block), L 100 (a partial 8-token block)
+    in 7 chunks of 16 tokens, so the adjoint carries cross 6 chunk boundaries."""
     x = make_case(11, 2, 40, 100)
     if not flags["softplus"]:
         # without softplus Delta = raw + bias must stay positive for a decaying recurrence
         x["delta"] = np.abs(x["delta"]) * 0.05 + 0.01
         x["delta_bias"][:] = 0.01
     print(f"[flags] {flags}", flush=True)
-    g = gpu_bwd(x, torch.float32, **flags)
+    g = gpu_bwd(x, torch.float32, chunk_len=16, **flags)
     r = ref_bwd(x, **flags)
     compare(g, r, 1e-4, f"flags {flags}", use_D=flags["use_D"], use_z=flags["use_z"],
             use_bias=flags["use_bias"])

@@ -79,13 +79,13 @@ FLAGS = [dict(softplus=s, use_D=d, use_z=z, use_bias=b, use_cb=cb)
     k[4 if k.startswith("use_") else 0] if v else "-" for k, v in f.items()))
 def test_conv_flags(flags):
     """Every flag combination at (2, 40, 100): a partial channel block, a partial sub-tile and
-    7 automatic chunks, so the conv history crosses sub-tile, tile and chunk boundaries."""
+    7 chunks of 16 tokens, so the conv history crosses sub-tile, tile and chunk boundaries."""
     x = make_case(21, 2, 40, 100)
     if not flags["softplus"]:
         x["delta"] = np.abs(x["delta"]) * 0.05 + 0.01
         x["delta_bias"][:] = 0.01
     print(f"[flags] {flags}", flush=True)
-    check(run(x, torch.float32, **flags), ref(x, **flags), 1e-4, f"flags {flags}")
+    check(run(x, torch.float32, chunk_len=16, **flags), ref(x, **flags), 1e-4, f"flags {flags}")
 
 
 @pytest.mark.parametrize("width", [1, 2, 3, 4])
