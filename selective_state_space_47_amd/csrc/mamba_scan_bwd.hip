@@ -21,7 +21,8 @@
 //  1. (chunked only) forward chunk summaries -- the forward kernel in summary mode;
 //  2. checkpoints: the forward kernel in checkpoint mode stores h before every 8th token;
 //  3. (chunked only) adjoint chunk summaries: for every chunk but the first, the adjoint carry
-//     leaving the chunk's start when the carry entering at its end is zero, and its sum of Delta;
+//     leaving the chunk's start when the carry entering at its end is zero, and its sum of Delta
+//     (lam needs dy, C and Abar only, so this pass recomputes no state and reads no checkpoint);
 //  4. the main backward kernel: per 8-token block, last block first, recompute h and the readout
 //     from the checkpoint, then run the adjoint recurrence backwards through the block;
 //  5. deterministic reductions: dB, dC over the channel blocks of a sequence; dA, dD, dbias over
@@ -161,10 +162,14 @@ __global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
     int64_t ix = row + (ok ? t : t_end - 1), ick = (ch * p.nblk8 + jb) * kN + 2 * g,
             ibc = bcrow + min(tb + sq, t_end - 1);
     asm volatile("" : "+v"(ix), "+v"(ick), "+v"(ibc));
-    const float xl = ld_f32(U, ix), drl = ld_f32(DL, ix), gol = ld_f32(GO, ix);
+    // the adjoint summary needs neither u nor B nor the recomputed state (lam depends on dy, C
+    // and Abar only)
+    const float xl = kSum ? 0.f : ld_f32(U, ix);
+    const float drl = ld_f32(DL, ix), gol = ld_f32(GO, ix);
     const float zl = kGate ? ld_f32(Z, ix) : 0.f;
-    const float2 hs = *reinterpret_cast<const float2*>(p.ckpt + ick);
-    const float bcl = srB ? ld_f32(Bm, ibc) : ld_f32(Cm, ibc);
+    const float2 hs = kSum ? make_float2(0.f, 0.f)
+                           : *reinterpret_cast<const float2*>(p.ckpt + ick);
+    const float bcl = srB ? (kSum ? 0.f : ld_f32(Bm, ibc)) : ld_f32(Cm, ibc);
     const float x = ok ? xl : 0.f;
     const float draw = ok ? drl : 0.f;
     const float zv = ok ? zl : 0.f;
@@ -186,7 +191,19 @@ __global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
 
     // ---- recompute h over the block from its checkpoint; partial readouts
     float e0[kBT], e1[kBT], hh0[kBT], hh1[kBT];
-    {
+    if (kSum) {
+      // adjoint summary: the block's Abar and dy only
+#pragma unroll
+      for (int tl = 0; tl < kBT; ++tl) {
+        const float2 q = *reinterpret_cast<const float2*>(&sm.dd[w][tl][c]);
+        e0[tl] = fast_exp2(q.x * a0);
+        e1[tl] = fast_exp2(q.x * a1);
+      }
+      float dy = go;
+      if (kGate) dy = go * zv * __builtin_amdgcn_rcpf(1.f + fast_exp2(-zv * kLog2e));
+      reinterpret_cast<float*>(&sm.dd[w][g][c])[2] = dy;
+      wave_lds_fence();
+    } else {
       float h0 = hs.x, h1 = hs.y;
       float(*ys)[kSYs] = sm.scr[w].y;
 #pragma unroll
@@ -213,10 +230,8 @@ __global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
         dy = go * zv * s;
         dzv = go * ypre * s * fmaf(zv, 1.f - s, 1.f);
       }
-      if (!kSum) {
-        dDacc = fmaf(dy, x, dDacc);
-        if (kGate && ok && dvalid) st_out(static_cast<Tin*>(p.dz), ix, dzv);
-      }
+      dDacc = fmaf(dy, x, dDacc);
+      if (kGate && ok && dvalid) st_out(static_cast<Tin*>(p.dz), ix, dzv);
       reinterpret_cast<float*>(&sm.dd[w][g][c])[2] = dy;
       wave_lds_fence();
     }
