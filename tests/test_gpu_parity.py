@@ -437,3 +437,68 @@ def test_bf16_output_rounding_is_nearest_even():
     y32b, _ = gpu_scan(xb, torch.float32, use_z=False)
     ybf, _ = gpu_scan(xb, torch.bfloat16, use_z=False)
     assert np.array_equal(ybf, synth.round_to_bf16(y32b.astype(np.float32)))
+
+
+# --------------------------------------------------------------------- maximum sizes
+
+def _device_case(seed, batch, dim, L, io):
+    """Seeded inputs drawn on the device (the sizes here are too large for the host generator);
+    the oracle reads back exactly these values."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    t = {k: torch.randn((batch, dim, L), generator=g, device=DEV).to(io)
+         for k in ("u", "delta", "z")}
+    for k in ("B", "C"):
+        t[k] = torch.randn((batch, 16, L), generator=g, device=DEV).to(io)
+    p = synth.random_case(seed, 1, dim, 1)
+    for k in ("A", "D", "delta_bias"):
+        t[k] = dev(p[k])
+    return t
+
+
+@pytest.mark.parametrize("io,L", [(torch.float32, (1 << 25) - 1), (torch.bfloat16, (1 << 26) - 8)],
+                         ids=["fp32-2^25-1", "bf16-2^26-8"])
+def test_max_seqlen(io, L):
+    """The longest sequences the 32-bit row offsets allow (32 rows of a workgroup times L times
+    the element size stays below 2^32).  33 channels put the last row of a partial channel block
+    at the largest offsets.  Channels 0 and 32 are compared with the oracle over every token."""
+    print(f"[max seqlen] {io} L={L}", flush=True)
+    t = _device_case(48, 1, 33, L, io)
+    out, last = binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                       t["delta_bias"], True, return_last_state=True)
+    torch.cuda.synchronize()
+    chs = [0, 32]
+    host = {k: t[k][:, chs].float().cpu().numpy() for k in ("u", "delta", "z")}
+    host.update({k: t[k].float().cpu().numpy() for k in ("B", "C")})
+    host.update({k: t[k][chs].cpu().numpy() for k in ("A", "D", "delta_bias")})
+    y = out[:, chs].float().cpu().numpy()
+    fin = last[:, chs].cpu().numpy()
+    del t, out, last
+    torch.cuda.empty_cache()
+    ry, rl = ref_scan(host)
+    # fp32: the long-sequence bound max|y - ref| <= 1e-3 rms(ref); bf16 output: 1e-2 relative
+    # with the rms floor (rounding error scales with |y|)
+    bf = io == torch.bfloat16
+    e_y = rel_err(y, ry) if bf else rel_err(y, ry, "rms")
+    e_s = rel_err(fin, rl)
+    tol = 1e-2 if bf else 1e-3
+    print(f"[max seqlen] rel err y {e_y:.3e} last_state {e_s:.3e}", flush=True)
+    assert np.isfinite(y).all() and e_y <= tol and e_s <= tol
+
+
+def test_state_update_max_batch():
+    """65535 sequences, the largest batch of the state update; every output and state checked."""
+    batch, dim = 65535, 8
+    w = synth.random_case(49, batch, dim, 1, bf16=True)
+    rng = np.random.default_rng(49)
+    st0 = rng.standard_normal((batch, dim, 16)).astype(np.float32)
+    u, dl, z = (w[k][:, :, 0] for k in ("u", "delta", "z"))
+    B, C = w["B"][:, :, 0], w["C"][:, :, 0]
+    state = dev(st0)
+    bf = torch.bfloat16
+    y = binding.mamba_state_update(state, dev(u, bf), dev(dl, bf), dev(w["A"]), dev(B, bf),
+                                   dev(C, bf), dev(w["D"]), dev(z, bf), dev(w["delta_bias"]), True)
+    torch.cuda.synchronize()
+    ry, rs = oracle.state_update_ref(st0, u, dl, w["A"], B, C, w["D"], z, w["delta_bias"], True)
+    assert rel_err(y.float().cpu().numpy(), ry) <= 1e-2
+    assert rel_err(state.cpu().numpy(), rs) <= 1e-4
