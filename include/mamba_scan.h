@@ -67,6 +67,7 @@ enum mamba_status {
  * always fp32.  Arithmetic is always fp32; bf16 outputs are rounded to nearest, ties to even. */
 enum mamba_dtype { MAMBA_F32 = 0, MAMBA_BF16 = 1 };
 
+/* batch * dim * seqlen is at most 2^40 elements (MAMBA_ERR_SHAPE otherwise). */
 typedef struct mamba_dims {
   int64_t batch;     /* number of sequences, >= 1 */
   int64_t dim;       /* channels D, >= 1 */
@@ -202,13 +203,17 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
  *       C 8-byte aligned)
  * A, B and C hold bf16 values (16-bit storage).  Requirements (MAMBA_ERR_SHAPE / _ALIGN otherwise):
  * M % 16 == 0, N % 8 == 0, K % 8 == 0, lda and ldb multiples of 8, A and B 16-byte aligned,
- * 1 <= batch <= 65535.  C must not overlap A or B.
+ * 1 <= batch <= 65535; M, N, K, lda, ldb and ldc below 2^31, b_bstride and c_bstride in
+ * [0, 2^40).  C must not overlap A or B.
  */
 int mamba_gemm_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                     int64_t batch, int64_t lda, int64_t ldb, int64_t b_bstride, int64_t ldc,
                     int64_t c_bstride, int b_kcontig, int c_trans, void* stream);
 
-/* Sizes of a Mamba block (mamba_block_fwd). */
+/* Sizes of a Mamba block (mamba_block_fwd).  seqlen, d_model, d_inner and dt_rank are at most
+ * 2^30, batch * seqlen * 2 * d_inner and batch * seqlen * d_model at most 2^40, and seqlen stays
+ * within the scan's bound for bf16 (seqlen < 2^26); MAMBA_ERR_SHAPE otherwise, before anything is
+ * launched. */
 typedef struct mamba_block_dims {
   int64_t batch;      /* sequences, 1..65535 */
   int64_t seqlen;     /* tokens L, a multiple of 8 */
