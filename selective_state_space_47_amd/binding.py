@@ -148,6 +148,21 @@ def _raise(status):
         raise ValueError(f"mamba library error {status}: {mamba_status_string(status)}")
 
 
+def _workspace(workspace, need, dev, min_bytes=0):
+    """The caller's workspace, checked, or a new one of `need` bytes (at least min_bytes).
+    Returns (tensor or None, its size in bytes)."""
+    if workspace is None:
+        n = max(need, min_bytes)
+        if n == 0:
+            return None, 0
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
                    return_last_state=False, chunk_len=0, out=None, last_state=None,
                    workspace=None):
@@ -181,14 +196,13 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
     L_ = lib()
     ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_ptr = _ptr(workspace)
-    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    st = L_.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                           _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
-                           _ptr(last_state), ctypes.byref(dm), ws_ptr, ws_len, stream)
+    workspace, ws_len = _workspace(workspace, ws_bytes, dev)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = L_.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
+                               _ptr(last_state), ctypes.byref(dm), _ptr(workspace), ws_len,
+                               stream)
     _raise(st)
     return (out, last_state) if return_last_state else out
 
@@ -234,15 +248,14 @@ def mamba_scan_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bi
     dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
     L_ = lib()
     ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    st = L_.mamba_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(width),
-                                _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
-                                _ptr(last_state), _ptr(u_out), ctypes.byref(dm),
-                                _ptr(workspace), ws_len, stream)
+    workspace, ws_len = _workspace(workspace, ws_bytes, dev)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = L_.mamba_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(width),
+                                    _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                    _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
+                                    _ptr(last_state), _ptr(u_out), ctypes.byref(dm),
+                                    _ptr(workspace), ws_len, stream)
     _raise(st)
     res = [out]
     if return_last_state:
@@ -280,10 +293,12 @@ def mamba_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _check(out, "out", (batch, dim), io, dev)
     dm = make_dims(batch, dim, 1, code, DSTATE, 0)
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    st = lib().mamba_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                  _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
-                                  _ptr(out), ctypes.byref(dm), stream)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = lib().mamba_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                      _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                      int(bool(delta_softplus)), _ptr(out), ctypes.byref(dm),
+                                      stream)
     _raise(st)
     return out
 
@@ -342,15 +357,15 @@ def mamba_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
     L_ = lib()
     ws_bytes = int(L_.mamba_scan_bwd_workspace_bytes(ctypes.byref(dm)))
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    ws_len = workspace.numel() * workspace.element_size()
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    st = L_.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                           _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dout), _ptr(dlast),
-                           _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
-                           _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
-                           ctypes.byref(dm), _ptr(workspace), ws_len, stream)
+    workspace, ws_len = _workspace(workspace, ws_bytes, dev, min_bytes=1)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = L_.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dout),
+                               _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                               _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                               _ptr(g["ddelta_bias"]), ctypes.byref(dm), _ptr(workspace),
+                               ws_len, stream)
     _raise(st)
     return {k: g[k] for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias")}
 
@@ -375,9 +390,10 @@ def mamba_gemm_bf16(A, B, b_kcontig=True, c_trans=False, out=None):
     _check(out, "out", shape, torch.bfloat16, dev)
     ldb = K if b_kcontig else N
     ldc = M if c_trans else N
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    st = lib().mamba_gemm_bf16(_ptr(A), _ptr(B), _ptr(out), M, N, K, batch, K, ldb, N * K,
-                               ldc, M * N, int(bool(b_kcontig)), int(bool(c_trans)), stream)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = lib().mamba_gemm_bf16(_ptr(A), _ptr(B), _ptr(out), M, N, K, batch, K, ldb, N * K,
+                                   ldc, M * N, int(bool(b_kcontig)), int(bool(c_trans)), stream)
     _raise(st)
     return out
 
@@ -427,12 +443,12 @@ def mamba_block_fwd(hidden, w_in, conv_weight, conv_bias, w_x, w_dt, dt_bias, A,
     dm = block_dims(hidden, w_in, w_x, w_dt, conv_weight)
     L_ = lib()
     ws_bytes = int(L_.mamba_block_workspace_bytes(ctypes.byref(dm)))
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    ws_len = workspace.numel() * workspace.element_size()
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    st = L_.mamba_block_fwd(_ptr(hidden), _ptr(w_in), _ptr(conv_weight), _ptr(conv_bias),
-                            _ptr(w_x), _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(w_out),
-                            _ptr(out), ctypes.byref(dm), _ptr(workspace), ws_len, stream)
+    workspace, ws_len = _workspace(workspace, ws_bytes, dev, min_bytes=1)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = L_.mamba_block_fwd(_ptr(hidden), _ptr(w_in), _ptr(conv_weight), _ptr(conv_bias),
+                                _ptr(w_x), _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D),
+                                _ptr(w_out), _ptr(out), ctypes.byref(dm), _ptr(workspace),
+                                ws_len, stream)
     _raise(st)
     return out

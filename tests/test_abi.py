@@ -231,3 +231,15 @@ def test_gemm_validation_codes(lib):
     assert gemm(K=2 ** 31, lda=2 ** 31, ldb=2 ** 31) == -2
     assert gemm(bs=2 ** 40) == -2 and gemm(bs=-8) == -2 and gemm(cs=2 ** 40) == -2
     assert gemm(ldc=2 ** 31) == -2
+
+
+def test_binding_workspace_checks():
+    """The binding refuses a workspace that is not a contiguous tensor on the inputs' device,
+    before anything reaches the library."""
+    import torch
+    dev = torch.device("cuda:0")
+    assert binding._workspace(None, 0, dev) == (None, 0)
+    with pytest.raises(ValueError):
+        binding._workspace(torch.empty(64, dtype=torch.uint8), 16, dev)      # host memory
+    with pytest.raises(TypeError):
+        binding._workspace(bytearray(64), 16, dev)

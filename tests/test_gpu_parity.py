@@ -502,3 +502,12 @@ def test_state_update_max_batch():
     ry, rs = oracle.state_update_ref(st0, u, dl, w["A"], B, C, w["D"], z, w["delta_bias"], True)
     assert rel_err(y.float().cpu().numpy(), ry) <= 1e-2
     assert rel_err(state.cpu().numpy(), rs) <= 1e-4
+
+
+def test_host_workspace_is_refused():
+    x = synth.random_case(50, 1, 40, 300)
+    t = {k: dev(v) for k, v in x.items()}
+    with pytest.raises(ValueError):
+        binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                               t["delta_bias"], True, chunk_len=64,
+                               workspace=torch.empty(1 << 20, dtype=torch.uint8))
