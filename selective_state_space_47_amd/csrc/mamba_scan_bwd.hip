@@ -84,8 +84,10 @@ __device__ __forceinline__ float tree8(const float* v) {
 }
 
 // kSum = true: adjoint chunk summary (pass 3); false: the gradients (pass 4).
-template <typename Tin, bool kSum, bool kSoftplus, bool kGate>
-__global__ __launch_bounds__(kThreads, 5) void scan_bwd_kernel(BwdArgs p) {
+// kOcc: workgroups per CU the register budget is cut for.  5 (96 VGPRs, a few values spilled)
+// when the grid fills 5 per CU; 4 (no spills) when it gives at most 4 per CU anyway.
+template <typename Tin, bool kSum, bool kSoftplus, bool kGate, int kOcc>
+__global__ __launch_bounds__(kThreads, kOcc) void scan_bwd_kernel(BwdArgs p) {
   __shared__ BwdSmem sm;
   const Tin* __restrict__ U = static_cast<const Tin*>(p.u);
   const Tin* __restrict__ DL = static_cast<const Tin*>(p.delta);
@@ -416,10 +418,22 @@ BwdLayout bwd_layout(const mamba_dims* dm, const Plan& pl) {
   return o;
 }
 
+// Grids of at most this many workgroups leave at most 4 per CU on 256 CUs (measured: the
+// 130M-layer backward, 768 workgroups, 262 -> 233 us with the unspilled kernel; at 1280
+// workgroups the 5-per-CU kernel is 4% faster).
+constexpr unsigned kFewWG = 4 * 256;
+
 template <typename Tin, bool kSum, bool kSoftplus, bool kGate>
 int launch_bwd_one(dim3 grid, hipStream_t s, const BwdArgs& a) {
-  hipLaunchKernelGGL((scan_bwd_kernel<Tin, kSum, kSoftplus, kGate>), grid, dim3(kThreads), 0, s,
-                     a);
+  if constexpr (!kSum) {
+    if (grid.x <= kFewWG) {
+      hipLaunchKernelGGL((scan_bwd_kernel<Tin, kSum, kSoftplus, kGate, 4>), grid, dim3(kThreads),
+                         0, s, a);
+      return launch_status();
+    }
+  }
+  hipLaunchKernelGGL((scan_bwd_kernel<Tin, kSum, kSoftplus, kGate, 5>), grid, dim3(kThreads), 0,
+                     s, a);
   return launch_status();
 }
 
