@@ -30,6 +30,7 @@
 //    summary (prod Abar = exp(A * sum Delta), h_local).  The main kernel composes the summaries
 //    of all earlier chunks in order to get its carry-in state, then runs its chunk.
 #include "mamba_common.h"
+#include <type_traits>
 
 namespace mamba {
 
@@ -255,8 +256,18 @@ struct ScanThread {
   }
 };
 
+// Register budget: 5 workgroups per CU (96 VGPRs).  The fp32 main pass with the gate or the
+// fused conv does not fit and spilled 13-27 values there; it is compiled for 4 per CU instead
+// (no spills: 130M-layer 68 -> 61 us, 2^17 tokens 1745 -> 1640 us, 2^20 tokens 15.0 -> 14.8 ms;
+// the bf16 instances fit and keep 5).
+template <typename Tin, int kMode, bool kGate, bool kConv>
+constexpr int scan_occupancy() {
+  return (std::is_same<Tin, float>::value && kMode == kModeMain && (kGate || kConv)) ? 4 : 5;
+}
+
 template <typename Tin, int kMode, bool kVec, bool kSoftplus, bool kGate, bool kConv>
-__global__ __launch_bounds__(kThreads, 5) void scan_kernel(ScanArgs p) {
+__global__ __launch_bounds__(kThreads, (scan_occupancy<Tin, kMode, kGate, kConv>()))
+void scan_kernel(ScanArgs p) {
   constexpr bool kMain = kMode == kModeMain || kMode == kModeMainT;
   __shared__ ScanSmem sm;
   ScanThread<Tin, kMode, kVec, kSoftplus, kGate, kConv> th(sm);
