@@ -162,3 +162,9 @@ def test_conv_workload_2p8b_layer_sampled():
     print(f"[2p8b_layer conv] {len(chs)} channels: out {e[0]:.2e} last {e[1]:.2e} u {e[2]:.2e}",
           flush=True)
     assert e.max() <= 1e-2
+
+
+def test_conv_fp32_between_one_and_two_rounds():
+    """fp32 fused conv at 1280 workgroups, unchunked (one full round of the GPU)."""
+    x = make_case(23, 4, 10240, 64)
+    check(run(x, torch.float32), ref(x), 1e-4, "fp32 conv, 1280 workgroups")

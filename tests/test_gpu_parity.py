@@ -511,3 +511,15 @@ def test_host_workspace_is_refused():
         binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
                                t["delta_bias"], True, chunk_len=64,
                                workspace=torch.empty(1 << 20, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("batch,dim,L", [(4, 10240, 64), (2, 32768, 40)],
+                         ids=["1280-workgroups", "2048-workgroups"])
+def test_fp32_gated_between_one_and_two_rounds(batch, dim, L):
+    """fp32 with the gate at grids between one and two rounds of the GPU (1280 and 2048
+    workgroups, unchunked; the second with a scalar tail, L % 8 != 0); compared in full with the
+    oracle."""
+    x = synth.random_case(51, batch, dim, L)
+    y, last = gpu_scan(x, torch.float32)
+    ry, rl = ref_scan(x)
+    assert rel_err(y, ry) <= 1e-4 and rel_err(last, rl) <= 1e-4
