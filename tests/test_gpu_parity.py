@@ -523,3 +523,39 @@ def test_fp32_gated_between_one_and_two_rounds(batch, dim, L):
     y, last = gpu_scan(x, torch.float32)
     ry, rl = ref_scan(x)
     assert rel_err(y, ry) <= 1e-4 and rel_err(last, rl) <= 1e-4
+
+
+def test_side_streams_run_concurrently():
+    """Work goes on the caller's current stream: two scans with their own workspaces (chunked)
+    and a state update, issued on two side streams without synchronizing in between, each
+    match the oracle."""
+    xa = synth.random_case(52, 2, 96, 700)
+    xb = synth.random_case(53, 1, 70, 1000, bf16=True)
+    ta = {k: dev(v) for k, v in xa.items()}
+    tb = {k: dev(v, torch.bfloat16 if k in ("u", "delta", "z", "B", "C") else torch.float32)
+          for k, v in xb.items()}
+    st0 = np.random.default_rng(54).standard_normal((2, 96, 16)).astype(np.float32)
+    state = dev(st0)
+    t0 = {k: ta[k][:, :, 0].contiguous() for k in ("u", "delta", "z", "B", "C")}
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        ya, la = binding.mamba_scan_fwd(ta["u"], ta["delta"], ta["A"], ta["B"], ta["C"], ta["D"],
+                                        ta["z"], ta["delta_bias"], True, return_last_state=True,
+                                        chunk_len=64)
+        ys = binding.mamba_state_update(state, t0["u"], t0["delta"], ta["A"], t0["B"], t0["C"],
+                                        ta["D"], t0["z"], ta["delta_bias"], True)
+    with torch.cuda.stream(s2):
+        yb, lb = binding.mamba_scan_fwd(tb["u"], tb["delta"], tb["A"], tb["B"], tb["C"], tb["D"],
+                                        tb["z"], tb["delta_bias"], True, return_last_state=True,
+                                        chunk_len=128)
+    s1.synchronize()
+    s2.synchronize()
+    ry, rl = ref_scan(xa)
+    assert rel_err(ya.cpu().numpy(), ry) <= 1e-4 and rel_err(la.cpu().numpy(), rl) <= 1e-4
+    ry, rl = ref_scan(xb)
+    assert rel_err(yb.float().cpu().numpy(), ry) <= 1e-2 and rel_err(lb.cpu().numpy(), rl) <= 1e-2
+    u0, d0, z0 = (xa[k][:, :, 0] for k in ("u", "delta", "z"))
+    ry, rs = oracle.state_update_ref(st0, u0, d0, xa["A"], xa["B"][:, :, 0], xa["C"][:, :, 0],
+                                     xa["D"], z0, xa["delta_bias"], True)
+    assert rel_err(ys.cpu().numpy(), ry) <= 1e-4 and rel_err(state.cpu().numpy(), rs) <= 1e-4
