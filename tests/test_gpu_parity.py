@@ -559,3 +559,47 @@ def test_side_streams_run_concurrently():
     ry, rs = oracle.state_update_ref(st0, u0, d0, xa["A"], xa["B"][:, :, 0], xa["C"][:, :, 0],
                                      xa["D"], z0, xa["delta_bias"], True)
     assert rel_err(ys.cpu().numpy(), ry) <= 1e-4 and rel_err(state.cpu().numpy(), rs) <= 1e-4
+
+
+def test_graph_capture_replays_match_eager():
+    """The entry points allocate nothing and issue no memsets, so they can be captured in a HIP
+    graph: a chunked scan (with its workspace) and an in-place state update, replayed three times
+    with eager work in between, match the eager results bitwise on every replay."""
+    x = synth.random_case(55, 2, 64, 300)
+    t = {k: dev(v) for k, v in x.items()}
+    t0 = {k: t[k][:, :, 0].contiguous() for k in ("u", "delta", "z", "B", "C")}
+    st0 = dev(np.random.default_rng(55).standard_normal((2, 64, 16)).astype(np.float32))
+    nws = binding.mamba_scan_workspace_bytes(2, 64, 300, torch.float32, chunk_len=64)
+    assert nws > 0
+
+    def run(out, last, ws, state):
+        binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                               t["delta_bias"], True, return_last_state=True, chunk_len=64,
+                               out=out, last_state=last, workspace=ws)
+        return binding.mamba_state_update(state, t0["u"], t0["delta"], t["A"], t0["B"], t0["C"],
+                                          t["D"], t0["z"], t["delta_bias"], True)
+
+    bufs = lambda: (torch.empty_like(t["u"]), torch.empty((2, 64, 16), device=DEV),
+                    torch.empty(nws, dtype=torch.uint8, device=DEV), st0.clone())
+    e_out, e_last, e_ws, e_state = bufs()
+    e_y = run(e_out, e_last, e_ws, e_state)
+    torch.cuda.synchronize()
+    g_out, g_last, g_ws, g_state = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # warm-up outside the capture
+        run(g_out, g_last, g_ws, g_state)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_y = run(g_out, g_last, g_ws, g_state)
+    for rep in range(3):
+        g_out.fill_(float(rep + 7))                    # eager work between replays
+        g_last.fill_(-1.0)
+        g_state.copy_(st0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_out, e_out) and torch.equal(g_last, e_last), rep
+        assert torch.equal(g_y, e_y) and torch.equal(g_state, e_state), rep
