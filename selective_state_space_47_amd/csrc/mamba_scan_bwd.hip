@@ -238,7 +238,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void scan_bwd_kernel(BwdArgs p) {
       wave_lds_fence();
     }
 
-    // ---- adjoint recurrence backwards through the block
+    // ---- adjoint recurrence backwards through the block, at raised wave issue priority (the
+    // 2.8B-layer backward 1% faster; the same around the recompute loop was 5% slower)
+    __builtin_amdgcn_s_setprio(1);
     float ta[kBT], gb[kBT];
 #pragma unroll
     for (int tl = kBT - 1; tl >= 0; --tl) {
@@ -274,6 +276,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void scan_bwd_kernel(BwdArgs p) {
       __builtin_amdgcn_sched_barrier(0);  // bound LDS-read hoisting (register pressure)
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (!kSum) {
       // ---- token g: sums over the channel's 8 lanes, then du and dDelta_raw
       float(*tg)[kTGs] = sm.scr[w].tg;
