@@ -634,11 +634,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs p) {
   else store_tile(p.dst[0]);
 }
 
-// imbalance of t equal tiles over the CUs: the busiest CU's share over the mean
-double tile_imbalance(int64_t t) {
+// rounds of t equal tiles over the CUs (one large-tile workgroup per CU)
+int64_t tile_rounds(int64_t t) {
   const int64_t cus = 256;
-  const int64_t rounds = (t + cus - 1) / cus;
-  return (double)(rounds * cus) / (double)t;
+  return (t + cus - 1) / cus;
 }
 
 // K step and stage count of the large-tile kernel
@@ -710,7 +709,10 @@ int launch_gemm(const GemmArgs& a, bool b_kcontig, int64_t batch, hipStream_t s)
     const int64_t mt = (a.M + 255) / 256;
     const int64_t t256 = mt * ((a.N + 255) / 256) * batch;
     const int64_t t128 = mt * ((a.N + 127) / 128) * batch;
-    if (tile_imbalance(t256) <= tile_imbalance(t128) * 1.05)
+    // A 256-wide tile costs about 1.6 times a 128-wide one (in_proj in whole rounds: 737 against
+    // 918 us) while moving fewer bytes per flop; take it unless its rounds cost more.  out_proj
+    // (640 or 1280 tiles) runs 390 us with 256-wide tiles against 440 us with 128-wide ones.
+    if (16 * tile_rounds(t256) <= 10 * tile_rounds(t128))
       return launch_big<256, kBigBK, kBigStages>(a, batch, s);
     return launch_big<128, kBigBK, kBigStages>(a, batch, s);
   }
