@@ -202,3 +202,16 @@ def test_bwd_workload_2p8b_layer_full_compare():
     print("[2p8b_layer] gpu done; oracle", flush=True)
     r = ref_bwd(x)
     compare(g, r, 1e-2, "2p8b_layer")
+
+
+def test_bwd_long_sequence_chunks():
+    """A long sequence over few channels: the automatic plan cuts 2^17 tokens of 768 channels
+    into 64 chunks of 2048 (the long-sequence branch), so the adjoint carries cross 63 chunk
+    boundaries; every gradient compared with the oracle at full size."""
+    # 17 floats per channel for every chunk but the last: 64 chunks
+    assert binding.mamba_scan_workspace_bytes(1, 768, 1 << 17, torch.float32) == 768 * 63 * 17 * 4
+    x = make_case(18, 1, 768, 1 << 17)
+    print("[long chunks] (1, 768, 2^17), 64 chunks", flush=True)
+    g = gpu_bwd(x, torch.float32)
+    r = ref_bwd(x)
+    compare(g, r, 1e-4, "long chunks")
