@@ -357,6 +357,8 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(const float* __restrict_
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   const float* pp = part + ((b * dblocks) * L + t) * 32 + 8 * jq;
+  // unrolled so that several blocks' loads are in flight; the sums stay in block order
+#pragma unroll 4
   for (int32_t blk = 0; blk < dblocks; ++blk) {
     const float4 v0 = *reinterpret_cast<const float4*>(pp);
     const float4 v1 = *reinterpret_cast<const float4*>(pp + 4);
