@@ -117,8 +117,12 @@ struct ScanThread {
     const bool ok0 = t < t_end, ok1 = t + 1 < t_end;
     rbc[0] = load_pair<kVec>(at(Bs + t0, bofs), 0, ok0, ok1);
     rbc[1] = load_pair<kVec>(at(Bs + L + t0, bofs), 0, ok0, ok1);
-    rbc[2] = load_pair<kVec>(at(Cs + t0, bofs), 0, ok0, ok1);
-    rbc[3] = load_pair<kVec>(at(Cs + L + t0, bofs), 0, ok0, ok1);
+    if (kMode == kModeMain || kMode == kModeMainT) {
+      rbc[2] = load_pair<kVec>(at(Cs + t0, bofs), 0, ok0, ok1);
+      rbc[3] = load_pair<kVec>(at(Cs + L + t0, bofs), 0, ok0, ok1);
+    } else {  // the summary and checkpoint passes have no readout: C is staged as zeros
+      rbc[2] = rbc[3] = Raw{};
+    }
   }
   // prefetch of sub-tile s of the tile starting at tn (uniform branch)
   __device__ __forceinline__ void prefetch_sub(int64_t tn, int s) {
