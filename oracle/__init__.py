@@ -140,6 +140,24 @@ def state_update_ref(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return out, st
 
 
+def state_update_ref_inplace(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                             delta_softplus=False):
+    """state_update_ref that updates `state` (a C-contiguous float64 array (batch, dim, N)) in
+    place instead of copying it; returns out (batch, dim) in float64."""
+    assert isinstance(state, np.ndarray) and state.dtype == np.float64
+    assert state.flags["C_CONTIGUOUS"] and state.ndim == 3
+    u, delta, A, B, C = (_f64(v) for v in (u, delta, A, B, C))
+    D, z, delta_bias = _f64(D), _f64(z), _f64(delta_bias)
+    batch, dim, N = state.shape
+    assert u.shape == (batch, dim) and delta.shape == (batch, dim)
+    assert A.shape == (dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
+    out = np.empty((batch, dim), dtype=np.float64)
+    _load().ref_state_update_f64(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                                 batch, dim, N, _ptr(out))
+    return out
+
+
 def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
                  dout=None, dlast=None):
     """Gradients of sum(out * dout) + sum(last_state * dlast) by the hand-written adjoint
@@ -153,7 +171,7 @@ def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     D, z, delta_bias, dout, dlast = (_f64(v) for v in (D, z, delta_bias, dout, dlast))
     batch, dim, L = u.shape
     N = A.shape[1]
-    assert N <= 64 and dout is not None and dout.shape == u.shape
+    assert dout is not None and dout.shape == u.shape
     assert dlast is None or dlast.shape == (batch, dim, N)
     assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
     res = {k: np.empty(s, dtype=np.float64) for k, s in (

@@ -181,12 +181,12 @@ void ref_scan_bwd_f64(const double* u, const double* delta, const double* A, con
     double* sig = (double*)malloc((size_t)L * sizeof(double));
     double* ypre = (double*)malloc((size_t)L * sizeof(double));
     double* lam = (double*)malloc((size_t)N * sizeof(double));
+    double* gA = (double*)malloc((size_t)N * sizeof(double));
 #pragma omp for schedule(static)
     for (int64_t d = 0; d < dim; ++d) {
       const double* Arow = A + d * N;
       const double bias = delta_bias ? delta_bias[d] : 0.0;
       const double Dd = D ? D[d] : 0.0;
-      double gA[64];
       for (int64_t n = 0; n < N; ++n) gA[n] = 0.0;
       double gD = 0.0, gbias = 0.0;
       for (int64_t b = 0; b < batch; ++b) {
@@ -246,6 +246,7 @@ void ref_scan_bwd_f64(const double* u, const double* delta, const double* A, con
     free(sig);
     free(ypre);
     free(lam);
+    free(gA);
   }
   for (int64_t i = 0; i < nbc; ++i) {
     double sb = 0.0, sc = 0.0;

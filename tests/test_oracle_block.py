@@ -66,3 +66,59 @@ def test_block_causal_prefix():
     full = block.block_ref(**synth.block_inputs(w))
     pre = block.block_ref(**synth.block_inputs(w, seqlen=16))
     np.testing.assert_allclose(pre, full[:, :16], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ the block oracle's bf16 rounding
+
+def test_nearest_bf16_ties_go_to_even():
+    """Halfway cases: 1 + 2^-8 lies between 1 and 1 + 2^-7 and goes to the even 1; 1 + 3*2^-8 lies
+    between 1 + 2^-7 and 1 + 2^-6 and goes to the even 1 + 2^-6; the same for negatives and at
+    other binades; a hair past a tie rounds away from it."""
+    q = 2.0 ** -8
+    x = np.array([1 + q, 1 + 3 * q, -(1 + q), -(1 + 3 * q), (1 + q) * 2.0 ** 40,
+                  (1 + 3 * q) * 2.0 ** -100, 1 + q + 2.0 ** -40, 1 + q - 2.0 ** -40])
+    want = np.array([1.0, 1 + 2 * 2 * q, -1.0, -(1 + 4 * q), 2.0 ** 40, (1 + 4 * q) * 2.0 ** -100,
+                     1 + 2 * q, 1.0])
+    np.testing.assert_array_equal(block.nearest_bf16(x), want)
+
+
+def test_nearest_bf16_special_values():
+    x = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0])
+    r = block.nearest_bf16(x)
+    assert np.isnan(r[0]) and np.isnan(r[1])
+    assert r[2] == np.inf and r[3] == -np.inf
+    assert r[4] == 0.0 and not np.signbit(r[4]) and r[5] == 0.0 and np.signbit(r[5])
+    # a NaN among finite values stays a NaN and leaves its neighbours alone
+    r = block.nearest_bf16(np.array([1.5, np.nan, -2.25]))
+    assert r[0] == 1.5 and np.isnan(r[1]) and r[2] == -2.25
+
+
+def test_nearest_bf16_range_ends():
+    big = (2 - 2.0 ** -7) * 2.0 ** 127                  # largest finite bf16
+    half_ulp = 2.0 ** (127 - 8)
+    r = block.nearest_bf16(np.array([big, big + half_ulp * 0.99, big + half_ulp, -big - half_ulp,
+                                     1e300]))
+    assert r[0] == big and r[1] == big
+    assert r[2] == np.inf and r[3] == -np.inf and r[4] == np.inf  # the tie goes to the even 2^128
+    # subnormal spacing 2^-133: ties at the bottom go to even multiples
+    s = 2.0 ** -133
+    r = block.nearest_bf16(np.array([s, 0.5 * s, 1.5 * s, 2.5 * s, 0.49 * s, 3 * s * 2 ** -126]))
+    np.testing.assert_array_equal(r, [s, 0.0, 2 * s, 2 * s, 0.0, 0.0])
+
+
+def test_nearest_bf16_matches_torch_on_float32_values():
+    """On values that are exactly float32, rounding from float64 equals torch's own float32 ->
+    bfloat16 conversion (round to nearest, ties to even), an independent library routine."""
+    import torch
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    f32 = bits.view(np.float32)
+    f32 = f32[np.isfinite(f32)]
+    ref = torch.from_numpy(f32.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(block.nearest_bf16(f32.astype(np.float64)), ref)
+    # and on a dense set of ties and near-ties around a few binades
+    base = np.array([1.0, 3.0, 2.0 ** -126, 2.0 ** 100], dtype=np.float64)
+    k = np.arange(-300, 300, dtype=np.float64)
+    near = (base[:, None] * (1 + k[None, :] * 2.0 ** -16)).astype(np.float32).ravel()
+    ref = torch.from_numpy(near.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(block.nearest_bf16(near.astype(np.float64)), ref)
