@@ -62,20 +62,27 @@ def test_block_small(shape):
     assert np.isfinite(out).all() and e <= 2e-2
 
 
-def test_block_2p8b_first_tokens():
+@pytest.mark.timeout(400)
+def test_block_2p8b_full():
     """The Mamba-2.8B layer sizes at full length (8 x 2048 tokens) in the benchmark's
-    configuration; the oracle computes the first 64 tokens of every sequence (causality: they
-    depend on nothing later) and the rest is checked finite."""
+    configuration; every output of every token of every sequence compared with the block oracle
+    (its projections as float64 BLAS products)."""
     w = synth.BLOCK_WORKLOADS["block_2p8b"]
     p = synth.block_inputs(w)
     print(f"[block_2p8b] batch={w.batch} L={w.seqlen} d_model={w.d_model} E={w.d_inner}",
           flush=True)
     out = run(p)
+    print("[block_2p8b] GPU done", flush=True)
     assert np.isfinite(out).all()
-    pre = synth.block_inputs(w, seqlen=64)
-    ref = block.block_ref(**pre)
-    e = rel_err(out[:, :64], ref)
-    print(f"[block_2p8b] first 64 tokens rel err {e:.2e}", flush=True)
+    es = []
+    for b in range(w.batch):
+        q = dict(p)
+        q["hidden"] = p["hidden"][b:b + 1]
+        ref = block.block_ref(**q)
+        es.append(rel_err(out[b:b + 1], ref))
+        print(f"[block_2p8b] sequence {b}: rel err {es[-1]:.2e}", flush=True)
+    e = max(es)
+    print(f"[block_2p8b] all {w.batch} x {w.seqlen} tokens: rel err {e:.2e}", flush=True)
     assert e <= 2e-2
 
 

@@ -130,9 +130,11 @@ def test_conv_width_validation():
         binding.mamba_scan_fwd_conv(t["u"], w5, t["delta"], t["A"], t["B"], t["C"])
 
 
-def test_conv_workload_2p8b_layer_sampled():
-    """The 2.8B-layer shape (bf16) with width-4 taps: the full run, oracle on sampled channels
-    (conv and scan of each sampled channel's rows)."""
+@pytest.mark.timeout(300)
+def test_conv_workload_2p8b_layer_full():
+    """The 2.8B-layer shape (bf16) with width-4 taps: the full run, and every output, final state
+    and conv output u of every channel compared with the oracle (conv then scan, one sequence per
+    oracle call)."""
     w = synth.WORKLOADS["2p8b_layer"]
     x = synth.scan_inputs(w)
     cw, cb = synth.conv_params(w, 4)
@@ -144,24 +146,21 @@ def test_conv_workload_2p8b_layer_sampled():
         dev["D"], dev["z"], dev["delta_bias"], True, conv_bias=torch.from_numpy(cb).to(DEV),
         return_last_state=True, return_u=True)
     torch.cuda.synchronize()
+    del dev
     out, last, u = out.float().cpu().numpy(), last.cpu().numpy(), u.float().cpu().numpy()
-    assert np.isfinite(out).all() and np.isfinite(last).all()
-    rng = np.random.default_rng(3)
-    chs = np.unique(np.concatenate([rng.choice(w.channels, 96, replace=False),
-                                    [0, w.channels - 1, w.dim - 1, w.dim]]))
-    errs = []
-    for ch in chs:
-        b, d = divmod(int(ch), w.dim)
-        o, s, uu = oracle.scan_conv_ref(x["u"][b:b + 1, d:d + 1], cw[d:d + 1], cb[d:d + 1],
-                                        x["delta"][b:b + 1, d:d + 1], x["A"][d:d + 1],
-                                        x["B"][b:b + 1], x["C"][b:b + 1], x["D"][d:d + 1],
-                                        x["z"][b:b + 1, d:d + 1], x["delta_bias"][d:d + 1], True)
-        errs.append((rel_err(out[b, d], o[0, 0]), rel_err(last[b, d], s[0, 0]),
-                     rel_err(u[b, d], uu[0, 0])))
-    e = np.max(np.array(errs), axis=0)
-    print(f"[2p8b_layer conv] {len(chs)} channels: out {e[0]:.2e} last {e[1]:.2e} u {e[2]:.2e}",
-          flush=True)
-    assert e.max() <= 1e-2
+    print("[2p8b_layer conv] GPU done", flush=True)
+    ro = np.empty(out.shape, dtype=np.float64)
+    rs = np.empty(last.shape, dtype=np.float64)
+    ru = np.empty(u.shape, dtype=np.float64)
+    for b in range(w.batch):
+        o, s, uu = oracle.scan_conv_ref(x["u"][b:b + 1], cw, cb, x["delta"][b:b + 1], x["A"],
+                                        x["B"][b:b + 1], x["C"][b:b + 1], x["D"],
+                                        x["z"][b:b + 1], x["delta_bias"], True)
+        ro[b], rs[b], ru[b] = o[0], s[0], uu[0]
+    e = (rel_err(out, ro), rel_err(last, rs), rel_err(u, ru))
+    print(f"[2p8b_layer conv] all {w.channels} channels: out {e[0]:.2e} last {e[1]:.2e} "
+          f"u {e[2]:.2e}", flush=True)
+    assert max(e) <= 1e-2
 
 
 def test_conv_fp32_between_one_and_two_rounds():

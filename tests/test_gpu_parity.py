@@ -86,116 +86,100 @@ def test_workload_full_compare(name):
     assert e_y <= 1e-4 and e_s <= 1e-4
 
 
-def _sample_channels(nch, k, seed):
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(nch, size=min(k, nch), replace=False).tolist())
-    pick.update({0, nch - 1, nch // 2})
-    return np.array(sorted(pick), dtype=np.int64)
-
-
-def test_workload_2p8b_layer_sampled():
-    """Full-size bf16 run in the benchmark's launch configuration; oracle on sampled channels."""
+@pytest.mark.timeout(400)
+def test_workload_2p8b_layer_full():
+    """Full-size bf16 run in the benchmark's launch configuration; every output of every channel
+    and every final state compared with the oracle (one sequence per oracle call)."""
     w = synth.WORKLOADS["2p8b_layer"]
     x = synth.scan_inputs(w)
     print(f"[2p8b_layer] batch={w.batch} dim={w.dim} L={w.seqlen} bf16", flush=True)
     y, last = gpu_scan(x, torch.bfloat16)
-    assert np.isfinite(y).all() and np.isfinite(last).all()
-    chs = _sample_channels(w.channels, 192, 1)
-    y2 = y.reshape(w.channels, w.seqlen)[chs]
-    l2 = last.reshape(w.channels, 16)[chs]
-    b = chs // w.dim
-    d = chs % w.dim
-    # oracle per sampled channel: gather its rows, its sequence's B/C and its parameters
-    sub = dict(u=x["u"].reshape(-1, w.seqlen)[chs][:, None, :],
-               delta=x["delta"].reshape(-1, w.seqlen)[chs][:, None, :],
-               z=x["z"].reshape(-1, w.seqlen)[chs][:, None, :])
-    ry = np.empty_like(y2, dtype=np.float64)
-    rl = np.empty_like(l2, dtype=np.float64)
-    for i in range(len(chs)):
-        o, s = oracle.scan_ref(sub["u"][i:i + 1], sub["delta"][i:i + 1], x["A"][d[i]:d[i] + 1],
-                               x["B"][b[i]:b[i] + 1], x["C"][b[i]:b[i] + 1], x["D"][d[i]:d[i] + 1],
-                               sub["z"][i:i + 1], x["delta_bias"][d[i]:d[i] + 1], True)
-        ry[i], rl[i] = o[0, 0], s[0, 0]
-    e_y, e_s = rel_err(y2, ry), rel_err(l2, rl)
-    print(f"[2p8b_layer] {len(chs)} channels: rel err out {e_y:.3e} last_state {e_s:.3e}",
+    print("[2p8b_layer] GPU done", flush=True)
+    ry = np.empty(y.shape, dtype=np.float64)
+    rl = np.empty(last.shape, dtype=np.float64)
+    for b in range(w.batch):
+        ry[b], rl[b] = [r[0] for r in oracle.scan_ref(
+            x["u"][b:b + 1], x["delta"][b:b + 1], x["A"], x["B"][b:b + 1], x["C"][b:b + 1],
+            x["D"], x["z"][b:b + 1], x["delta_bias"], True)]
+    e_y, e_s = rel_err(y, ry), rel_err(last, rl)
+    print(f"[2p8b_layer] all {w.channels} channels: rel err out {e_y:.3e} last_state {e_s:.3e}",
           flush=True)
     assert e_y <= 1e-2 and e_s <= 1e-2
 
 
-def test_workload_1m_steps_sampled():
-    """Million-token fp32 sequence (cross-chunk carry); oracle on sampled channels,
-    bound 1e-3 * rms."""
+@pytest.mark.timeout(400)
+def test_workload_1m_steps_full():
+    """Million-token fp32 sequence (cross-chunk carry), all 1536 channels compared with the
+    oracle over every token, streamed in blocks of 128 channels; bound max|err| <= 1e-3 * rms
+    over the whole output (and the same form for last_state)."""
     w = synth.WORKLOADS["1m_steps"]
-    chs = _sample_channels(w.channels, 13, 3)
     print(f"[1m_steps] dim={w.dim} L={w.seqlen}: generating", flush=True)
     x = synth.scan_inputs(w)
     t = {k: dev(v) for k, v in x.items()}
-    del x["u"], x["delta"], x["z"]
     out, last = binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
                                        t["delta_bias"], True, return_last_state=True)
     torch.cuda.synchronize()
+    del t
     print("[1m_steps] GPU done", flush=True)
-    idx = torch.from_numpy(chs).to(DEV)
-    y = out.reshape(w.channels, w.seqlen).index_select(0, idx).cpu().numpy()
-    lst = last.reshape(w.channels, 16).index_select(0, idx).cpu().numpy()
-    assert torch.isfinite(out).all().item()
-    del t, out
-    torch.cuda.empty_cache()
-    sub = synth.scan_inputs(w, channels=chs)
-    ry, rl = oracle.scan_ref(sub["u"][None], sub["delta"][None], x["A"][chs % w.dim],
-                             x["B"], x["C"], x["D"][chs % w.dim], sub["z"][None],
-                             x["delta_bias"][chs % w.dim], True)
-    e_y = rel_err(y, ry[0], "rms")
-    e_s = rel_err(lst, rl[0], "rms")
-    print(f"[1m_steps] {len(chs)} channels: err out {e_y:.3e} rms, last_state {e_s:.3e} rms",
+    lst = last.reshape(w.dim, 16).cpu().numpy()
+    max_e = max_es = 0.0
+    ss = ss_s = 0.0
+    blk = 128
+    rl_all = np.empty((w.dim, 16), dtype=np.float64)
+    for c0 in range(0, w.dim, blk):
+        c1 = min(w.dim, c0 + blk)
+        ry, rl = oracle.scan_ref(x["u"][:, c0:c1], x["delta"][:, c0:c1], x["A"][c0:c1], x["B"],
+                                 x["C"], x["D"][c0:c1], x["z"][:, c0:c1],
+                                 x["delta_bias"][c0:c1], True)
+        yb = out[0, c0:c1].cpu().numpy().astype(np.float64)
+        assert np.isfinite(yb).all()
+        max_e = max(max_e, float(np.max(np.abs(yb - ry[0]))))
+        ss += float(np.sum(ry[0] * ry[0]))
+        rl_all[c0:c1] = rl[0]
+        print(f"[1m_steps] channels {c0}..{c1 - 1} compared", flush=True)
+    rms = math.sqrt(ss / (w.dim * w.seqlen))
+    e_y = max_e / rms
+    e_s = rel_err(lst, rl_all, "rms")
+    print(f"[1m_steps] all {w.dim} channels: err out {e_y:.3e} rms, last_state {e_s:.3e} rms",
           flush=True)
     assert e_y <= 1e-3 and e_s <= 1e-3
 
 
-def test_workload_gen_step_sampled():
-    """256 x 5120 fp32 states, 1000 in-place bf16 steps; y of every step and the final state
-    checked on sampled channels (24 channels in each of 4 sequences)."""
+@pytest.mark.timeout(400)
+def test_workload_gen_step_full():
+    """256 x 5120 fp32 states, 1000 in-place bf16 steps; every step's y of every channel of every
+    sequence and the final state of every channel compared with the oracle stepping the same
+    tokens (bound per step: R15 with that step's rms)."""
     w = synth.WORKLOADS["gen_step"]
     print(f"[gen_step] batch={w.batch} dim={w.dim} steps={w.steps}: generating", flush=True)
     x = synth.step_inputs(w)
-    rng = np.random.default_rng(4)
-    seqs = [0, 97, 255, int(rng.integers(1, 255))]
-    dsel = [np.sort(rng.choice(w.dim, 24, replace=False)) for _ in seqs]
-    chs = np.concatenate([b * w.dim + ds for b, ds in zip(seqs, dsel)])
-    idx = torch.from_numpy(chs).to(DEV)
     st = dev(x["state0"])
     A, D, bias = dev(x["A"]), dev(x["D"]), dev(x["delta_bias"])
     tok = {k: dev(x[k], torch.bfloat16) for k in ("u", "delta", "z", "B", "C")}
-    ys = torch.empty((w.steps, len(chs)), dtype=torch.float32, device=DEV)
-    out = torch.empty((w.batch, w.dim), dtype=torch.bfloat16, device=DEV)
+    ys = torch.empty((w.steps, w.batch, w.dim), dtype=torch.bfloat16, device=DEV)
     for s in range(w.steps):
         binding.mamba_state_update(st, tok["u"][s], tok["delta"][s], A, tok["B"][s], tok["C"][s],
-                                   D, tok["z"][s], bias, True, out=out)
-        ys[s] = out.reshape(-1).index_select(0, idx).float()
+                                   D, tok["z"][s], bias, True, out=ys[s])
     torch.cuda.synchronize()
+    del tok
     print("[gen_step] GPU done", flush=True)
-    y = ys.cpu().numpy()
-    fin = st.reshape(-1, 16).index_select(0, idx).cpu().numpy()
-    del tok, st
-    ref_y = np.empty(y.shape, dtype=np.float64)
-    ref_fin = []
-    col = 0
-    for b, ds in zip(seqs, dsel):
-        k = len(ds)
-        state = x["state0"][b, ds][None].astype(np.float64)          # (1, k, N)
-        for s in range(w.steps):
-            o, state = oracle.state_update_ref(state, x["u"][s, b, ds][None],
-                                               x["delta"][s, b, ds][None], x["A"][ds],
-                                               x["B"][s, b][None], x["C"][s, b][None], x["D"][ds],
-                                               x["z"][s, b, ds][None], x["delta_bias"][ds], True)
-            ref_y[s, col:col + k] = o[0]
-        ref_fin.append(state[0])
-        col += k
-    e_y = rel_err(y, ref_y)
-    e_s = rel_err(fin, np.concatenate(ref_fin))
-    print(f"[gen_step] {len(chs)} channels x {w.steps} steps: rel err y {e_y:.3e} "
+    fin = st.cpu().numpy()
+    # bf16 outputs as raw bits; widened to fp32 per step below
+    ybits = ys.view(torch.int16).cpu().numpy()
+    del ys, st
+    state = np.ascontiguousarray(x["state0"], dtype=np.float64)
+    worst = 0.0
+    for s in range(w.steps):
+        ref = oracle.state_update_ref_inplace(state, x["u"][s], x["delta"][s], x["A"], x["B"][s],
+                                              x["C"][s], x["D"], x["z"][s], x["delta_bias"], True)
+        got = (ybits[s].astype(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        worst = max(worst, rel_err(got, ref))
+        if s % 100 == 99:
+            print(f"[gen_step] step {s + 1}: worst rel err so far {worst:.3e}", flush=True)
+    e_s = rel_err(fin, state)
+    print(f"[gen_step] {w.channels} channels x {w.steps} steps: rel err y {worst:.3e} "
           f"state {e_s:.3e}", flush=True)
-    assert e_y <= 1e-2 and e_s <= 1e-2
+    assert worst <= 1e-2 and e_s <= 1e-2
 
 
 # --------------------------------------------------------------------- edge shapes and flags
