@@ -7,9 +7,13 @@ seeded synthetic data resident in HBM before timing starts.  The single-token st
 the generation workload (256 x 5120 x 16 fp32 states, bf16 tokens) is timed in the same run and
 reported in its own field.
 
-Prints one JSON line.  Roofline: the scan is bound by VALU issue on gfx950 (ALU_PEAK_LANE_OPS and
-ALU_OPS_PER_CHANNEL_STEP below give the peak and the per-channel-step op count); the HBM figure
-the metric names is reported next to it.
+Prints one JSON line.  Roofline: `roofline` is the HBM roofline the metric names (algorithmic
+bytes per launch over the scan kernel's mean HIP-event time, against 8 TB/s); the scan is bound
+by VALU issue on gfx950, and the ALU fraction (ALU_PEAK_LANE_OPS, ALU_OPS_PER_CHANNEL_STEP below)
+sits beside it.  Before timing, launches run for --settle-seconds so the clocks are settled
+whatever --warmup says.  `parity` compares the timed run's outputs with the fp64 oracle outputs
+that the CPU-baseline leg computes on the same inputs; the run fails if they differ beyond the
+workload's bound.
 """
 from __future__ import annotations
 
@@ -123,12 +127,16 @@ def cpu_baseline(x, w, target_cpu_s):
     done = 0
     spent = 0.0
     passes = 0
+    refs = {}
     while spent * cores < target_cpu_s:
         for b in range(w.batch):
             t0 = time.perf_counter()
-            oracle.scan_ref(x["u"][b:b + 1], x["delta"][b:b + 1], x["A"], x["B"][b:b + 1],
-                            x["C"][b:b + 1], x["D"], x["z"][b:b + 1], x["delta_bias"], True)
+            ref = oracle.scan_ref(x["u"][b:b + 1], x["delta"][b:b + 1], x["A"], x["B"][b:b + 1],
+                                  x["C"][b:b + 1], x["D"], x["z"][b:b + 1], x["delta_bias"],
+                                  True)
             spent += time.perf_counter() - t0
+            if b not in refs:
+                refs[b] = ref
             done += w.dim * L
             if spent * cores >= target_cpu_s:
                 break
@@ -143,13 +151,53 @@ def cpu_baseline(x, w, target_cpu_s):
                     break
     except OSError:
         pass
-    return dict(value=done / spent, unit="channel-steps/s", cores=cores, kind="oracle",
+    return refs, dict(value=done / spent, unit="channel-steps/s", cores=cores, kind="oracle",
                 cpu_model=model, usable_cores=len(os.sched_getaffinity(0)),
                 sample=f"{seqs} sequences ({passes} pass(es) over the {w.batch} sequences) x "
                        f"{w.dim} channels x {L} tokens of the {w.name} workload ({done} "
                        f"channel-steps, {spent:.1f} s wall x {cores} threads = "
                        f"{spent * cores:.0f} s of CPU work, fp64, OpenMP over channels; input "
                        f"conversion to fp64 not timed)")
+
+
+def timed_output_parity(out_h, last_h, refs, bound):
+    """Error of the timed run's out and last_state against the oracle outputs of the sequences
+    the CPU baseline computed: R15's max relative error (floor rms of the reference) and
+    max|err| / rms(ref), over every compared element."""
+    import numpy as np
+    seqs = sorted(refs)
+    if not seqs:
+        return None
+    ro = np.concatenate([refs[b][0] for b in seqs])
+    rl = np.concatenate([refs[b][1] for b in seqs])
+    go = np.asarray(out_h[seqs], dtype=np.float64)
+    gl = np.asarray(last_h[seqs], dtype=np.float64)
+    res = {}
+    for key, g, r in (("out", go, ro), ("last_state", gl, rl)):
+        rms = float(np.sqrt(np.mean(r * r)))
+        err = np.abs(g - r)
+        res[f"max_rel_err_{key}"] = float(np.max(err / np.maximum(np.abs(r), rms)))
+        res[f"err_rms_ratio_{key}"] = float(np.max(err)) / rms
+    res["bound"] = bound
+    res["ok"] = bool(res["max_rel_err_out"] <= bound and res["max_rel_err_last_state"] <= bound)
+    res["compared"] = f"sequences {seqs[0]}..{seqs[-1]} ({len(seqs)} of {out_h.shape[0]}), all " \
+                      f"channels and tokens, against the fp64 oracle on the same inputs"
+    return res
+
+
+def settle(step, torch, seconds):
+    """Untimed launches until `seconds` of wall time have passed, so the clocks reach their
+    sustained state whatever --warmup says; returns (seconds spent, launches)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return el, n
 
 
 def bench_state_update(steps, torch, binding, synth, dev):
@@ -203,8 +251,11 @@ def device_inputs(w, dev, torch, L=None, seed=0):
     return t
 
 
-def time_forward(t, torch, binding, reps, warm):
-    """HIP-event time of whole mamba_scan_fwd calls (all of its launches) on the current stream."""
+def time_forward(t, torch, binding, reps, warm, flush=False):
+    """HIP-event time of whole mamba_scan_fwd calls (all of its launches) on the current stream;
+    returns (median ms, MALL-flushed median ms or None).  flush: also time `reps` calls that each
+    follow a 512 MB scratch write (outside the events), so no input is left in the 256 MB
+    Infinity Cache."""
     u = t["u"]
     out = torch.empty_like(u)
     last = torch.empty((u.shape[0], u.shape[1], 16), dtype=torch.float32, device=u.device)
@@ -215,6 +266,7 @@ def time_forward(t, torch, binding, reps, warm):
                                last_state=last)
     for _ in range(warm):
         call()
+    settle(call, torch, 0.2)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -225,7 +277,22 @@ def time_forward(t, torch, binding, reps, warm):
         b.record(stream)
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return ms[len(ms) // 2]
+    fl = None
+    if flush:
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device=u.device)
+        fms = []
+        for _ in range(reps):
+            scratch.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            fms.append(a.elapsed_time(b))
+        del scratch
+        fms.sort()
+        fl = fms[len(fms) // 2]
+    return ms[len(ms) // 2], fl
 
 
 def bwd_alg_bytes(batch, dim, L, N, s_io):
@@ -256,6 +323,7 @@ def bench_backward(w, torch, binding, dev, reps, warm):
     grads.update(call())
     for _ in range(warm):
         call()
+    settle(call, torch, 0.3)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -300,6 +368,7 @@ def bench_conv(w, torch, binding, synth, dev, reps, warm, plain_us):
                                     return_last_state=True, out=out, last_state=last)
     for _ in range(warm):
         call()
+    settle(call, torch, 0.3)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -344,6 +413,7 @@ def bench_block(torch, binding, synth, dev, reps, warm):
                                 workspace=ws)
     for _ in range(warm):
         call()
+    settle(call, torch, 0.3)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -377,7 +447,8 @@ def other_workloads(torch, binding, synth, dev):
         w = synth.WORKLOADS[name]
         t = device_inputs(w, dev, torch)
         reps, warm = (5, 2) if name == "1m_steps" else (30, 20)
-        ms = time_forward(t, torch, binding, reps, warm)
+        # the 130M-layer inputs (101 MB) fit the Infinity Cache: also timed after a flush
+        ms, fl = time_forward(t, torch, binding, reps, warm, flush=name == "130m_layer")
         s = 2 if w.io_dtype == "bf16" else 4
         nbytes = scan_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s, s)
         ws = binding.mamba_scan_workspace_bytes(w.batch, w.dim, w.seqlen, t["u"].dtype)
@@ -387,6 +458,9 @@ def other_workloads(torch, binding, synth, dev):
                          alu_frac=w.channel_steps * ALU_OPS_PER_CHANNEL_STEP / (ms * 1e-3)
                          / ALU_PEAK_LANE_OPS,
                          chunked=ws > 0)
+        if fl is not None:
+            res[name]["us_mall_flushed"] = fl * 1e3
+            res[name]["alg_GBps_mall_flushed"] = nbytes / (fl * 1e-3) / 1e9
         del t
         torch.cuda.empty_cache()
     sweep = []
@@ -394,7 +468,7 @@ def other_workloads(torch, binding, synth, dev):
     for lg in (11, 13, 15, 17, 19, 20):
         L = 1 << lg
         t = device_inputs(w, dev, torch, L=L, seed=lg)
-        ms = time_forward(t, torch, binding, 5 if lg >= 19 else 15, 3)
+        ms, _ = time_forward(t, torch, binding, 5 if lg >= 19 else 15, 3)
         sweep.append(dict(L=L, us=ms * 1e3, channel_steps_per_s=w.dim * L / (ms * 1e-3)))
         del t
         torch.cuda.empty_cache()
@@ -405,8 +479,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first (the clocks need ~0.1 s of load to settle)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps first")
+    ap.add_argument("--settle-seconds", type=float, default=0.5,
+                    help="then untimed launches for this long, whatever --warmup says (the "
+                         "clocks need ~0.1-0.3 s of load to settle)")
     ap.add_argument("--workload", default="2p8b_layer")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
@@ -478,6 +554,7 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    settle_s, settle_n = settle(step, torch, args.settle_seconds)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -496,6 +573,9 @@ def main():
     chsteps = w.batch * w.dim * w.seqlen
     value = args.steps * chsteps / wall
     ok = bool(torch.isfinite(out.float()).all().item())
+    # the timed run's outputs, for the comparison with the oracle below
+    out_h = out.float().cpu().numpy()
+    last_h = last.cpu().numpy()
 
     if args.calib_copy:
         # plain streaming copy of a known size for counter calibration: reads 1 GiB, writes
@@ -556,17 +636,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",  # arithmetic type; storage of u/Delta/z/B/C/out is bf16 (config)
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seqlen": w.seqlen, "io_dtype": w.io_dtype, "state_dtype": "f32",
                    "softplus": True, "delta_bias": True, "D": True, "z_gate": True,
                    "channel_steps": chsteps, "chunks": 1 if ws_bytes == 0 else "multi"},
-        "roofline": {"bound": "alu", "achieved": alu_achieved / 1e12,
-                     "peak": ALU_PEAK_LANE_OPS / 1e12, "unit": "T lane-op/s",
-                     "frac": alu_achieved / ALU_PEAK_LANE_OPS, "traffic": traffic,
+        "roofline": {"bound": "hbm", "achieved": hbm_achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": hbm_achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "scan_kernel<bf16, main>",
-                     "ops_per_channel_step": ALU_OPS_PER_CHANNEL_STEP},
+                     "alu": {"achieved": alu_achieved / 1e12, "peak": ALU_PEAK_LANE_OPS / 1e12,
+                             "unit": "T lane-op/s", "frac": alu_achieved / ALU_PEAK_LANE_OPS,
+                             "ops_per_channel_step": ALU_OPS_PER_CHANNEL_STEP},
+                     "limiter": "VALU issue: 16 exp2 and ~100 other fp32 lane-ops per "
+                                "channel-step put the ALU floor above the HBM time; the HBM "
+                                "fraction is the metric's, the ALU fraction is what bounds it"},
         "hbm": {"achieved_GBps": hbm_achieved, "peak_GBps": HBM_PEAK_GBS,
                 "frac": hbm_achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg_bytes,
                 "bytes_per_channel_step": alg_bytes / chsteps,
@@ -578,6 +662,8 @@ def main():
         "kernel_us_mall_flushed": {"median": flushed[len(flushed) // 2] * 1e3,
                                    "p10": flushed[1] * 1e3, "p90": flushed[-2] * 1e3},
         "outputs_finite": ok,
+        "settle_s": settle_s,
+        "settle_launches": settle_n,
     }
     if not args.no_conv:
         rec["conv_fused_forward"] = bench_conv(w, torch, binding, synth, dev, 30, 100,
@@ -592,11 +678,18 @@ def main():
         rec["state_update"] = bench_state_update(args.step_steps, torch, binding, synth, dev)
     if not args.no_others:
         rec["other_workloads"], rec["seqlen_sweep"] = other_workloads(torch, binding, synth, dev)
+    parity_ok = True
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_seconds)
+        refs, rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_seconds)
+        rec["parity"] = timed_output_parity(out_h, last_h, refs, w.tol)
+        parity_ok = rec["parity"] is None or rec["parity"]["ok"]
     else:
         rec["cpu_baseline"] = None
+        rec["parity"] = None
     print(json.dumps(rec), flush=True)
+    if not parity_ok:
+        print("timed outputs differ from the oracle beyond the bound", file=sys.stderr)
+        return 1
     return 0
 
 
