@@ -85,7 +85,11 @@ typedef struct mamba_dims {
 size_t mamba_scan_workspace_bytes(const mamba_dims* dims);
 
 /*
- * Selective-scan forward from a zero state over `seqlen` tokens.
+ * Selective-scan forward from a zero state over `seqlen` tokens: the layer maps the whole known
+ * sequence to an output of the same shape ("Mamba" (elemedex), "How it works": the discrete
+ * selective SSM with Delta, B, C per token; "Mamba" (visual-learn), "Training without stepping
+ * token by token": with every token known, the per-token affine updates are combined as a
+ * parallel scan instead of a token-by-token loop).
  *
  *   u, delta, z, out : (batch, dim, seqlen), seqlen innermost, io_dtype
  *   B, C             : (batch, dstate, seqlen), io_dtype; shared by all channels of a sequence
@@ -131,7 +135,9 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
 
 /*
  * One generation step for `batch` sequences: the state is read and updated in place and one
- * output per channel is written.
+ * output per channel is written ("Mamba" (visual-learn), "Training without stepping token by
+ * token": during generation the fixed-size state absorbs one new token at a time at the same
+ * cost per token; "Mamba" (elemedex), "How it works": the same discrete update as the scan).
  *
  *   state            : (batch, dim, dstate) fp32, updated in place
  *   u, delta, z, out : (batch, dim), io_dtype
@@ -192,7 +198,8 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
 
 /*
  * Batched bf16 matrix product on the matrix cores, for the learned projections of a Mamba block
- * ("Mamba" (visual-learn), "Simplifications and limits": a real block adds learned projections;
+ * ("Mamba" (visual-learn), "Simplifications and limits": the trained layer puts linear maps around
+ * the SSM;
  * "Mamba" (elemedex), "How it works": the block starts with a linear projection):
  *     C[b] (M x N) = A (M x K) * B[b] (K x N),  fp32 accumulation, bf16 output (RNE).
  *   A : row-major, element (m, k) at A[m*lda + k], lda >= K; shared by every b
@@ -234,8 +241,8 @@ size_t mamba_block_workspace_bytes(const mamba_block_dims* dims);
  * A whole Mamba block forward with caller-supplied (e.g. random) weights, sources: "Mamba"
  * (elemedex), "How it works" (linear projection, short convolution, selective SSM, multiplicative
  * gate); "State Spaces, Selectively -- Mamba" (papermap), ch.02 (Delta, B, C computed from the
- * token); "Mamba" (visual-learn), "Simplifications and limits" (learned projections, short
- * convolution, output gate).  Per sequence, with E = d_inner, R = dt_rank, N = dstate:
+ * token); "Mamba" (visual-learn), "Simplifications and limits" (trained linear maps around the
+ * SSM, a brief convolution ahead of it, gating behind it).  Per sequence, with E = d_inner, R = dt_rank, N = dstate:
  *     [x; z]          = W_in hidden^T                      W_in  (2E, d_model) bf16
  *     u               = silu(causal_conv1d(x) + conv_bias)  conv_weight (E, conv_width) fp32
  *     [dlow; B; C]    = W_x u                               W_x   (R + 2N, E) bf16

@@ -40,12 +40,5 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
-def emit_asm(out_path: str) -> None:
-    """Write the gfx950 assembly of the library (for inspection of the generated code)."""
-    cmd = [hipcc()] + [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")] + [
-        "--cuda-device-only", "-S", "-I", INCLUDE, "-o", out_path] + SOURCES
-    subprocess.run(cmd, check=True)
-
-
 if __name__ == "__main__":
     print(build(verbose=True))

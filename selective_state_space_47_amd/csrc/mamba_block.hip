@@ -4,8 +4,9 @@
 // Sources (by page title and section): "Mamba" (elemedex), "How it works" -- the block is a
 // linear projection, a short convolution, the selective SSM and a multiplicative gate, stacked
 // homogeneously; "State Spaces, Selectively -- Mamba" (papermap), ch.02 -- Delta, B and C are
-// computed from the token; "Mamba" (visual-learn), "Simplifications and limits" -- a real block
-// adds learned projections, a short convolution and an output gate.
+// computed from the token; "Mamba" (visual-learn), "Simplifications and limits" -- beyond the
+// bare recurrence, the trained layer surrounds the SSM with linear maps in and out, a brief
+// convolution ahead of it and gating behind it.
 //
 // Data flow for hidden (batch, L, d_model), d_inner = E, dt_rank = R, dstate = N = 16:
 //   1. in_proj   (MFMA GEMM): [x; z] (2E x L per sequence) = W_in (2E x d_model) * hidden^T;
