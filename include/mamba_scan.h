@@ -29,8 +29,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers (memory the caller allocated on the current HIP
- *     device).  The caller owns every buffer; the library allocates nothing, keeps no pointer
- *     after returning and holds no global state.
+ *     device).  The caller owns every buffer; the library allocates nothing and keeps no pointer
+ *     after returning.  Its only state is the fixed scratch array of mamba_scan_fwd_noalloc (one
+ *     per GPU, from module load to process exit) and that array's per-device address.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the default stream)
  *     and runs asynchronously.  Buffers must stay valid until the stream reaches the work.
  *     The library never synchronizes; device faults surface at the caller's synchronization.
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 3
+#define MAMBA_SCAN_ABI_VERSION 4
 
 enum mamba_status {
   MAMBA_OK = 0,
@@ -60,8 +61,12 @@ enum mamba_status {
   MAMBA_ERR_UNSUPPORTED = -4, /* dstate != 16, or conv_width outside 1..4 */
   MAMBA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size */
   MAMBA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes() query */
-  MAMBA_ERR_HIP = -7          /* the HIP runtime rejected a launch */
+  MAMBA_ERR_HIP = -7,         /* the HIP runtime rejected a launch or a call */
+  MAMBA_ERR_SCRATCH = -8      /* mamba_scan_fwd_noalloc: the plan needs more than its scratch */
 };
+
+/* Size of the fixed scratch array behind mamba_scan_fwd_noalloc (bytes, per GPU). */
+#define MAMBA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Storage type of u, delta, z, B, C and out.  A, D, delta_bias, last_state and state are
  * always fp32.  Arithmetic is always fp32; bf16 outputs are rounded to nearest, ties to even. */
@@ -110,6 +115,29 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    const float* D, const void* z, const float* delta_bias, int softplus_flag,
                    void* out, float* last_state, const mamba_dims* dims, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * mamba_scan_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * chunk records that mamba_scan_fwd keeps in the caller's workspace go to a fixed device array
+ * of MAMBA_NOALLOC_SCRATCH_BYTES inside the library instead; this entry point calls no hipMalloc,
+ * hipFree or allocating library routine.
+ *
+ *   arguments        : as for mamba_scan_fwd, minus workspace and workspace_bytes
+ *
+ * Returns MAMBA_ERR_SCRATCH, before anything is launched, when mamba_scan_workspace_bytes(dims)
+ * exceeds MAMBA_NOALLOC_SCRATCH_BYTES (long sequences with many channels; e.g. batch*dim*(chunks-1)
+ * above about 246,000 chunk records of 68 bytes).  The array of the CURRENT device is used, so
+ * `stream` must belong to the current device; its address is resolved on the first call on each
+ * device (MAMBA_ERR_HIP if that fails).  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (different streams, or threads without ordering) race and give
+ * wrong results.  Calls on one stream are ordered and safe.  Nothing in the array has to start
+ * at zero (each call writes every record before reading it); it keeps the last call's contents.
+ */
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* delta_bias,
+                           int softplus_flag, void* out, float* last_state,
+                           const mamba_dims* dims, void* stream);
 
 /*
  * mamba_scan_fwd with u = silu(causal_conv1d(x)), the short depthwise convolution and SiLU that

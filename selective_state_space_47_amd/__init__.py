@@ -7,7 +7,7 @@ marshal torch tensors into pointers and sizes.  Importing this package does not 
 library; the first call does, and raises if it has not been built.
 """
 
-__all__ = ["mamba_scan_fwd", "mamba_scan_fwd_conv", "mamba_state_update",
+__all__ = ["mamba_scan_fwd", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_conv", "mamba_state_update",
            "mamba_scan_workspace_bytes", "mamba_scan_bwd", "mamba_gemm_bf16",
            "mamba_block_fwd", "mamba_block_workspace_bytes", "mamba_scan_bwd_workspace_bytes", "mamba_status_string",
            "mamba_abi_version", "library_path"]

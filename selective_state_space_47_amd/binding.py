@@ -36,7 +36,7 @@ class mamba_dims(ctypes.Structure):
                 ("chunk_len", ctypes.c_int32)]
 
 
-EXPORTS = ("mamba_scan_fwd", "mamba_scan_fwd_conv", "mamba_state_update",
+EXPORTS = ("mamba_scan_fwd", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_conv", "mamba_state_update",
            "mamba_scan_workspace_bytes",
            "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_gemm_bf16",
            "mamba_block_fwd", "mamba_block_workspace_bytes", "mamba_status_string",
@@ -63,6 +63,9 @@ def lib():
             L.mamba_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp, fp, dp,
                                          vp, ctypes.c_size_t, vp]
             L.mamba_scan_fwd.restype = ctypes.c_int
+            L.mamba_scan_fwd_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, ctypes.c_int, vp,
+                                                 fp, dp, vp]
+            L.mamba_scan_fwd_noalloc.restype = ctypes.c_int
             L.mamba_scan_fwd_conv.argtypes = [vp, fp, fp, ctypes.c_int, vp, fp, vp, vp, fp, vp,
                                               fp, ctypes.c_int, vp, fp, vp, dp, vp,
                                               ctypes.c_size_t, vp]
@@ -203,6 +206,44 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
                                _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
                                _ptr(last_state), ctypes.byref(dm), _ptr(workspace), ws_len,
                                stream)
+    _raise(st)
+    return (out, last_state) if return_last_state else out
+
+
+def mamba_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                           delta_softplus=False, return_last_state=False, chunk_len=0, out=None,
+                           last_state=None):
+    """mamba_scan_fwd_noalloc of include/mamba_scan.h: the forward with its chunk records in the
+    library's fixed per-GPU scratch array (no workspace).  Arguments and results as for
+    mamba_scan_fwd; outputs are allocated here only when not passed in."""
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, L = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io = u.dtype
+    code = _io_code(io)
+    for t, name, shape, dt in ((u, "u", (batch, dim, L), io), (delta, "delta", (batch, dim, L), io),
+                               (z, "z", (batch, dim, L), io), (B, "B", (batch, DSTATE, L), io),
+                               (C, "C", (batch, DSTATE, L), io),
+                               (A, "A", (dim, DSTATE), torch.float32),
+                               (D, "D", (dim,), torch.float32),
+                               (delta_bias, "delta_bias", (dim,), torch.float32)):
+        _check(t, name, shape, dt, dev)
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _check(out, "out", (batch, dim, L), io, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, DSTATE), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, dim, DSTATE), torch.float32, dev)
+    dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = lib().mamba_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                          _ptr(D), _ptr(z), _ptr(delta_bias),
+                                          int(bool(delta_softplus)), _ptr(out), _ptr(last_state),
+                                          ctypes.byref(dm), stream)
     _raise(st)
     return (out, last_state) if return_last_state else out
 

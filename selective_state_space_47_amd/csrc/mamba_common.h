@@ -313,7 +313,7 @@ __attribute__((visibility("hidden"))) int scan_forward(
     const void* delta, const float* A, const void* B, const void* C, const float* D,
     const void* z, const float* delta_bias, int softplus_flag, void* out, float* last_state,
     const mamba_dims* dims, void* workspace, size_t workspace_bytes, void* stream,
-    bool out_tmajor);
+    bool out_tmajor, bool use_scratch = false);
 __attribute__((visibility("hidden"))) int launch_fwd(int mode, bool bf, bool vec, bool softplus,
                                                      bool gate, dim3 grid, hipStream_t s,
                                                      const ScanArgs& a);

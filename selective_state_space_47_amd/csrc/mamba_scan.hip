@@ -30,6 +30,7 @@
 //    summary (prod Abar = exp(A * sum Delta), h_local).  The main kernel composes the summaries
 //    of all earlier chunks in order to get its carry-in state, then runs its chunk.
 #include "mamba_common.h"
+#include <mutex>
 #include <type_traits>
 
 namespace mamba {
@@ -549,15 +550,46 @@ int mamba::launch_fwd(int mode, bool bf, bool vec, bool softplus, bool gate, dim
   }
 }
 
+// Scratch of the allocation-free forward (mamba_scan_fwd_noalloc): the chunk records of the
+// cross-chunk carry (per channel and chunk but the last: the sum of Delta and the chunk-local
+// final state) are kept here instead of in a caller workspace.  Each GPU the library runs on holds
+// its own copy from module load until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: host code uses the address resolved per device below.
+static __device__ __align__(256) unsigned char scratch[MAMBA_NOALLOC_SCRATCH_BYTES];
+
 namespace mamba {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once resolved
+
+// Device address of the current device's `scratch`, resolved on the first call on that device
+// (with the device current) and kept for later calls.
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MAMBA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MAMBA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MAMBA_OK;
+}
+
+}  // namespace
 
 // Forward, optionally with the fused conv (conv_w != NULL: `u` holds x).
 // out_tmajor: out is (batch, L, dim) (bf16, dim % 8 == 0, no conv; used by the block).
+// use_scratch: the chunk records go to the current device's `scratch` array (workspace and
+// workspace_bytes are ignored); plans that need more than it holds are refused.
 int scan_forward(const void* u, const float* conv_w, const float* conv_b, int conv_width,
                  void* u_out, const void* delta, const float* A, const void* B, const void* C,
                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
                  void* out, float* last_state, const mamba_dims* dims, void* workspace,
-                 size_t workspace_bytes, void* stream, bool out_tmajor) {
+                 size_t workspace_bytes, void* stream, bool out_tmajor, bool use_scratch) {
   int st = check_dims(dims, false);
   if (st != MAMBA_OK) return st;
   if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_NULL;
@@ -571,6 +603,16 @@ int scan_forward(const void* u, const float* conv_w, const float* conv_b, int co
   Plan pl;
   st = make_plan(dims, &pl);
   if (st != MAMBA_OK) return st;
+  if (use_scratch) {
+    if (pl.ws_bytes > (size_t)MAMBA_NOALLOC_SCRATCH_BYTES) return MAMBA_ERR_SCRATCH;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (pl.ws_bytes > 0) {
+      st = scratch_address(&workspace);
+      if (st != MAMBA_OK) return st;
+      workspace_bytes = MAMBA_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
     return MAMBA_ERR_WORKSPACE;
   if (pl.ws_bytes > 0 && !aligned(workspace, 4)) return MAMBA_ERR_ALIGN;
@@ -626,7 +668,15 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    size_t workspace_bytes, void* stream) {
   return scan_forward(u, nullptr, nullptr, 0, nullptr, delta, A, B, C, D, z, delta_bias,
                       softplus_flag, out, last_state, dims, workspace, workspace_bytes, stream,
-                      false);
+                      false, false);
+}
+
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* delta_bias,
+                           int softplus_flag, void* out, float* last_state,
+                           const mamba_dims* dims, void* stream) {
+  return scan_forward(u, nullptr, nullptr, 0, nullptr, delta, A, B, C, D, z, delta_bias,
+                      softplus_flag, out, last_state, dims, nullptr, 0, stream, false, true);
 }
 
 int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
@@ -639,7 +689,7 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
   if (conv_width < 1 || conv_width > 4) return MAMBA_ERR_UNSUPPORTED;
   return scan_forward(x, conv_weight, conv_bias, conv_width, u_out, delta, A, B, C, D, z,
                       delta_bias, softplus_flag, out, last_state, dims, workspace,
-                      workspace_bytes, stream, false);
+                      workspace_bytes, stream, false, false);
 }
 
 int mamba_state_update(float* state, const void* u, const void* delta, const float* A,
@@ -679,6 +729,8 @@ const char* mamba_status_string(int status) {
     case MAMBA_ERR_ALIGN: return "misaligned pointer";
     case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
     case MAMBA_ERR_HIP: return "HIP launch failed";
+    case MAMBA_ERR_SCRATCH:
+      return "the allocation-free forward needs more scratch than its fixed array holds";
     default: return "unknown status";
   }
 }

@@ -125,6 +125,16 @@ int main(void) {
   d = dims(2, 64, 16, 128, 0, -16);
   EXPECT(scan(&d, FAKE, NULL, 0), MAMBA_ERR_SHAPE);
 
+  /* the allocation-free forward: the same validation, and its scratch bound before any HIP call */
+  EXPECT(mamba_scan_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, NULL, 1, FAKE, NULL, NULL,
+                                NULL), MAMBA_ERR_NULL);
+  d = dims(2, 64, 16, 128, 7, 0);
+  EXPECT(mamba_scan_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, NULL, 1, FAKE, NULL, &d,
+                                NULL), MAMBA_ERR_DTYPE);
+  d = dims(1, 64, 16, (int64_t)1 << 16, MAMBA_F32, 16);
+  EXPECT(mamba_scan_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, NULL, 1, FAKE, NULL, &d,
+                                NULL), MAMBA_ERR_SCRATCH);
+
   /* workspace queries over a sweep of valid shapes and chunk lengths */
   for (int64_t b = 1; b <= 3; ++b)
     for (int64_t dim = 1; dim <= 130; dim += 43)

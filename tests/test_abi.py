@@ -33,11 +33,11 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mamba_abi_version() == 3
+    assert lib.mamba_abi_version() == 4
 
 
 def test_status_strings(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = binding.mamba_status_string(code)
         assert s and s != "unknown status"
     assert binding.mamba_status_string(5) == "unknown status"
@@ -55,6 +55,29 @@ def call_scan(lib, dm, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=Non
               out=FAKE, last=None, ws=None, ws_bytes=0):
     return lib.mamba_scan_fwd(u, delta, A, B, C, D, z, bias, 1, out, last,
                               ctypes.byref(dm) if dm is not None else None, ws, ws_bytes, None)
+
+
+def call_noalloc(lib, dm, u=FAKE, out=FAKE):
+    return lib.mamba_scan_fwd_noalloc(u, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, out, None,
+                                      ctypes.byref(dm) if dm is not None else None, None)
+
+
+def test_noalloc_validation_codes(lib):
+    """The allocation-free forward validates like mamba_scan_fwd and refuses, before touching the
+    GPU, a plan whose chunk records exceed its fixed scratch (16 MiB)."""
+    assert call_noalloc(lib, None) == -1
+    assert call_noalloc(lib, dims(), u=None) == -1
+    assert call_noalloc(lib, dims(dstate=8)) == -4
+    assert call_noalloc(lib, dims(chunk=24)) == -2
+    assert call_noalloc(lib, dims(), u=ODD) == -5
+    # 64 channels x 4095 chunk records of 68 bytes = 17.8 MB > 16 MiB
+    big = dims(batch=1, dim=64, seqlen=1 << 16, chunk=16)
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(big)) > 16 << 20
+    assert call_noalloc(lib, big) == -8
+    assert "scratch" in binding.mamba_status_string(-8)
+    # just below the limit the plan is accepted by validation (it then needs the GPU)
+    ok = dims(batch=1, dim=64, seqlen=3840 * 16, chunk=16)
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok)) <= 16 << 20
 
 
 def test_scan_validation_codes(lib):
