@@ -601,7 +601,7 @@ int scan_forward(const void* u, const float* conv_w, const float* conv_b, int co
       (u_out && !aligned(u_out, es)))
     return MAMBA_ERR_ALIGN;
   Plan pl;
-  st = make_plan(dims, &pl);
+  st = (conv_w || out_tmajor) ? make_plan(dims, &pl) : make_plan_fwd(dims, &pl);
   if (st != MAMBA_OK) return st;
   if (use_scratch) {
     if (pl.ws_bytes > (size_t)MAMBA_NOALLOC_SCRATCH_BYTES) return MAMBA_ERR_SCRATCH;
@@ -639,6 +639,19 @@ int scan_forward(const void* u, const float* conv_w, const float* conv_b, int co
                    (!a.u_out || aligned(a.u_out, 16));
   if (out_tmajor && (conv_w || !bf || !vec || dims->dim % 8 || !aligned(out, 16)))
     return MAMBA_ERR_UNSUPPORTED;
+  if (pl.ts) {
+    // chunk summaries (if any) on the 32-channel summary kernel, then the time-split main pass
+    const int64_t dblocks32 = (dims->dim + kChWG - 1) / kChWG;
+    if (pl.nchunks > 1) {
+      a.dblocks = (int32_t)dblocks32;
+      dim3 grid((unsigned)(dims->batch * dblocks32 * (pl.nchunks - 1)));
+      if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
+        return MAMBA_ERR_HIP;
+    }
+    a.dblocks = (int32_t)pl.dblocks;
+    dim3 grid((unsigned)(dims->batch * pl.dblocks * pl.nchunks));
+    return launch_fwd_ts(bf, vec, softplus_flag != 0, z != nullptr, grid, s, a);
+  }
   if (pl.nchunks > 1) {
     dim3 grid((unsigned)(nwg_ch * (pl.nchunks - 1)));
     if (launch_fwd(kModeSummary, bf, vec, softplus_flag != 0, false, grid, s, a) != MAMBA_OK)
@@ -656,10 +669,12 @@ using namespace mamba;
 extern "C" {
 
 size_t mamba_scan_workspace_bytes(const mamba_dims* dims) {
+  // enough for the plain forward's plan and for the fused-conv forward's (which keeps the
+  // whole-sequence kernel)
   if (check_dims(dims, false) != MAMBA_OK) return 0;
-  Plan pl;
-  if (make_plan(dims, &pl) != MAMBA_OK) return 0;
-  return pl.ws_bytes;
+  Plan pf, pc;
+  if (make_plan_fwd(dims, &pf) != MAMBA_OK || make_plan(dims, &pc) != MAMBA_OK) return 0;
+  return std::max(pf.ws_bytes, pc.ws_bytes);
 }
 
 int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,

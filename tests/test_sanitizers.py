@@ -14,12 +14,14 @@ import subprocess
 
 import pytest
 
+from selective_state_space_47_amd import _build
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SAN = os.path.join(HERE, "sanitize")
 ORACLE_C = os.path.join(ROOT, "oracle", "mamba_oracle.c")
 CSRC = os.path.join(ROOT, "selective_state_space_47_amd", "csrc")
-HIP_SOURCES = ["mamba_scan.hip", "mamba_scan_bwd.hip", "mamba_gemm.hip", "mamba_block.hip"]
+HIP_SOURCES = [os.path.basename(f) for f in _build.SOURCES]  # every source of the library
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 CLANG = os.path.join(ROCM, "llvm", "bin", "clang")

@@ -1,7 +1,7 @@
 """GPU test of the allocation-free forward (mamba_scan_fwd_noalloc through the C ABI): two calls
 in a row, the second on a smaller input, each compared bit for bit with mamba_scan_fwd (same
-kernels, caller workspace) and with the fp64 oracle at the workload bound.  Both shapes are
-chunked, so the chunk records really pass through the library's scratch array."""
+kernels, caller workspace) and with the fp64 oracle at the workload bound.  Every call forces a
+chunk length, so the chunk records really pass through the library's scratch array."""
 import os
 
 import numpy as np
@@ -38,21 +38,22 @@ def _inputs(name_or_case):
     return synth.random_case(*name_or_case), torch.float32
 
 
-@pytest.mark.parametrize("first,second", [("130m_layer", "tiny"),
-                                          ((5, 3, 70, 1000), (6, 1, 33, 200))],
+@pytest.mark.parametrize("first,second", [(("130m_layer", 256), ("tiny", 64)),
+                                          (((5, 3, 70, 1000), 96), ((6, 1, 33, 200), 32))],
                          ids=["130m_then_tiny", "ragged_cases"])
 def test_noalloc_matches_workspace_entry_point(first, second):
-    for case in (first, second):
+    for case, chunk in (first, second):
         x, io = _inputs(case)
-        print(f"[noalloc] case {case}: u {x['u'].shape} {io}", flush=True)
+        print(f"[noalloc] case {case} chunk_len {chunk}: u {x['u'].shape} {io}", flush=True)
         t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in x.items()}
         t = {k: (v.to(io) if k in ("u", "delta", "z", "B", "C") else v) for k, v in t.items()}
-        assert binding.mamba_scan_workspace_bytes(*x["u"].shape, io) > 0  # chunked: uses scratch
+        assert binding.mamba_scan_workspace_bytes(*x["u"].shape, io, chunk_len=chunk) > 0
         o1, l1 = binding.mamba_scan_fwd_noalloc(t["u"], t["delta"], t["A"], t["B"], t["C"],
                                                 t["D"], t["z"], t["delta_bias"], True,
-                                                return_last_state=True)
+                                                return_last_state=True, chunk_len=chunk)
         o2, l2 = binding.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
-                                        t["z"], t["delta_bias"], True, return_last_state=True)
+                                        t["z"], t["delta_bias"], True, return_last_state=True,
+                                        chunk_len=chunk)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
         ry, rl = oracle.scan_ref(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
