@@ -75,9 +75,11 @@ def step_alg_bytes(batch, dim, N, s_in, s_out):
     return batch * dim * (2 * N * 4 + 3 * s_in + s_out) + batch * 2 * N * s_in + dim * (N + 2) * 4
 
 
-def parse_counters(fetch_csv, write_csv, out_json, scan_bytes_alg):
-    """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into per-launch HBM
-    bytes for the scan kernel, scaled by the same counters on a plain device copy of 1 GiB."""
+def parse_counters(fetch_csv, write_csv, out_json, alg_bytes, kernel_filter, label):
+    """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into HBM bytes per
+    dispatch of every kernel whose name contains `kernel_filter`, each scaled by the same counter
+    on a plain device copy of 1 GiB in the same run (--calib-copy).  alg_bytes: algorithmic bytes
+    of one call of the workload (all of its kernels); the record compares their sum with it."""
     import csv
 
     def read(path, counter):
@@ -90,29 +92,35 @@ def parse_counters(fetch_csv, write_csv, out_json, scan_bytes_alg):
                 per.setdefault(name, []).append(float(r["Counter_Value"]))
         return per
 
-    res = {}
+    kernels = {}
+    scale = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         per = read(path, counter)
-        scan = [v for k, vs in per.items() if "scan_kernel" in k for v in vs]
-        # the calibration copy: torch.mul(a, 1.0, out=b) over 1 GiB (--calib-copy); its largest
-        # dispatches (smaller ones of the same kernel come from torch's own setup)
+        # the calibration copy: torch.mul(a, 1.0, out=b) over 1 GiB; its largest dispatches
+        # (smaller ones of the same kernel come from torch's own setup)
         copy_k = [k for k in per if "MulFunctor<float>" in k and "AUnaryFunctor" in k]
         copy = sorted(per[copy_k[0]])[-3:] if copy_k else []
-        if not scan or not copy:
-            raise SystemExit(f"{counter}: scan or copy kernel not found in {path}: {list(per)}")
-        scan_kib = sorted(scan)[len(scan) // 2]
+        sel = {k: v for k, v in per.items() if kernel_filter in k}
+        if not sel or not copy:
+            raise SystemExit(f"{counter}: kernel '{kernel_filter}' or the copy not found in {path}")
         copy_kib = sorted(copy)[len(copy) // 2]
         factor = (1 << 30) / (copy_kib * 1024.0)
-        res[counter] = dict(scan_kib_per_dispatch=scan_kib, copy_kib_per_dispatch=copy_kib,
-                            copy_bytes=1 << 30, scale=factor,
-                            scan_bytes_scaled=scan_kib * 1024.0 * factor)
-    total = res["FETCH_SIZE"]["scan_bytes_scaled"] + res["WRITE_SIZE"]["scan_bytes_scaled"]
-    doc = dict(kernel="scan_kernel<bf16, main> (2p8b_layer workload)",
-               source_hash=kernel_source_hash(), counters=res, traffic_bytes_per_launch=total,
-               algorithmic_bytes_per_launch=scan_bytes_alg,
-               traffic_over_algorithmic=total / scan_bytes_alg)
-    with open(out_json, "w") as f:
-        json.dump(doc, f, indent=1)
+        scale[counter] = dict(copy_kib_per_dispatch=copy_kib, copy_bytes=1 << 30, scale=factor)
+        for k, v in sel.items():
+            kib = sorted(v)[len(v) // 2]
+            kernels.setdefault(k, {})[counter] = dict(kib_per_dispatch=kib, dispatches=len(v),
+                                                      bytes_scaled=kib * 1024.0 * factor)
+    for k, v in kernels.items():
+        v["traffic_bytes"] = sum(v[c]["bytes_scaled"] for c in ("FETCH_SIZE", "WRITE_SIZE")
+                                 if c in v)
+    total = sum(v["traffic_bytes"] for v in kernels.values())
+    doc = dict(workload=label, kernel_filter=kernel_filter, source_hash=kernel_source_hash(),
+               calibration=scale, kernels=kernels, traffic_bytes_per_call=total,
+               algorithmic_bytes_per_call=alg_bytes, traffic_over_algorithmic=total / alg_bytes,
+               note="per-call traffic sums one dispatch of each listed kernel")
+    if out_json:
+        with open(out_json, "w") as f:
+            json.dump(doc, f, indent=1)
     print(json.dumps(doc, indent=1))
 
 
@@ -183,6 +191,17 @@ def timed_output_parity(out_h, last_h, refs, bound):
     res["compared"] = f"sequences {seqs[0]}..{seqs[-1]} ({len(seqs)} of {out_h.shape[0]}), all " \
                       f"channels and tokens, against the fp64 oracle on the same inputs"
     return res
+
+
+def calib_copy(torch, dev):
+    """Plain streaming copy of a known size for counter calibration: reads 1 GiB, writes 1 GiB
+    (an elementwise multiply by one)."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def settle(step, torch, seconds):
@@ -502,7 +521,17 @@ def main():
                     help="time only the backward (for profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE CSVs into per-kernel bytes")
+    ap.add_argument("--counter-kernel", default="scan_kernel",
+                    help="--parse-counters: kernel-name substring to report")
+    ap.add_argument("--counter-json", default=None,
+                    help="--parse-counters: output file (default: the headline's profile record "
+                             "for the 2p8b_layer scan kernel)")
+    ap.add_argument("--counter-alg", choices=("scan", "step", "bwd"), default="scan",
+                    help="--parse-counters: algorithmic bytes of which call")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the state update of the generation workload")
     args = ap.parse_args()
 
     from selective_state_space_47_amd import synth
@@ -512,7 +541,18 @@ def main():
     alg_bytes = scan_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s_io, s_io)
 
     if args.parse_counters:
-        parse_counters(args.parse_counters[0], args.parse_counters[1], PROFILE_COUNTERS, alg_bytes)
+        if args.counter_alg == "step":
+            ws = synth.WORKLOADS["gen_step"]
+            nb, label = step_alg_bytes(ws.batch, ws.dim, ws.dstate, 2, 2), "gen_step"
+        elif args.counter_alg == "bwd":
+            nb, label = bwd_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s_io), w.name + " bwd"
+        else:
+            nb, label = alg_bytes, w.name
+        out = args.counter_json
+        if out is None and w.name == "2p8b_layer" and args.counter_alg == "scan":
+            out = PROFILE_COUNTERS
+        parse_counters(args.parse_counters[0], args.parse_counters[1], out, nb,
+                       args.counter_kernel, label)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selective scan runs on a single MI355X here "
@@ -531,17 +571,30 @@ def main():
     if args.block_only:
         print(json.dumps(bench_block(torch, binding, synth, dev, 10, 5)), flush=True)
         return 0
+    if args.step_only:
+        print(json.dumps(bench_state_update(args.step_steps, torch, binding, synth, dev)),
+              flush=True)
+        if args.calib_copy:
+            calib_copy(torch, dev)
+        return 0
     if args.bwd_only:
         print(json.dumps(bench_backward(w, torch, binding, dev, args.bwd_steps,
                                         args.bwd_warmup)), flush=True)
+        if args.calib_copy:
+            calib_copy(torch, dev)
         return 0
 
-    x = synth.scan_inputs(w)
     io = torch.bfloat16 if bf else torch.float32
-    t = {}
-    for k, v in x.items():
-        tt = torch.from_numpy(v).to(dev)
-        t[k] = tt.to(io) if k in ("u", "delta", "z", "B", "C") else tt
+    if args.no_cpu:
+        # no oracle leg: seeded device-side inputs of the same shape and distributions
+        x = None
+        t = device_inputs(w, dev, torch)
+    else:
+        x = synth.scan_inputs(w)
+        t = {}
+        for k, v in x.items():
+            tt = torch.from_numpy(v).to(dev)
+            t[k] = tt.to(io) if k in ("u", "delta", "z", "B", "C") else tt
     out = torch.empty((w.batch, w.dim, w.seqlen), dtype=io, device=dev)
     last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
     ws_bytes = binding.mamba_scan_workspace_bytes(w.batch, w.dim, w.seqlen, io)
@@ -578,14 +631,7 @@ def main():
     last_h = last.cpu().numpy()
 
     if args.calib_copy:
-        # plain streaming copy of a known size for counter calibration: reads 1 GiB, writes
-        # 1 GiB (an elementwise multiply by one; the largest non-scan dispatch of this run)
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
-        del a, b
+        calib_copy(torch, dev)
 
     # the same kernel with the last-level cache (MALL, 256 MB) flushed before each launch by a
     # 512 MB scratch write outside the events: the cold-cache kernel time
@@ -622,7 +668,7 @@ def main():
         with open(PROFILE_COUNTERS) as f:
             prof = json.load(f)
         if prof.get("source_hash") == kernel_source_hash() and args.workload == "2p8b_layer":
-            traffic = prof["traffic_bytes_per_launch"]
+            traffic = prof["traffic_bytes_per_call"]
 
     rec = {
         "metric": "selective-scan B·D·L channel-steps/s + achieved HBM GB/s "
