@@ -270,7 +270,7 @@ def device_inputs(w, dev, torch, L=None, seed=0):
     return t
 
 
-def time_forward(t, torch, binding, reps, warm, flush=False):
+def time_forward(t, torch, binding, reps, warm, flush=False, graph=0):
     """HIP-event time of whole mamba_scan_fwd calls (all of its launches) on the current stream;
     returns (median ms, MALL-flushed median ms or None).  flush: also time `reps` calls that each
     follow a 512 MB scratch write (outside the events), so no input is left in the 256 MB
@@ -297,6 +297,32 @@ def time_forward(t, torch, binding, reps, warm, flush=False):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     fl = None
+    if graph:
+        # per-call time inside a replayed HIP graph of `graph` calls: no host launch overhead
+        # between calls (the entry points allocate nothing and issue no memsets, so they capture)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                call()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(graph):
+                call()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            gms.append(a.elapsed_time(b) / graph)
+        del g
+        graph_ms = sorted(gms)[len(gms) // 2]
     if flush:
         scratch = torch.empty(1 << 27, dtype=torch.float32, device=u.device)
         fms = []
@@ -311,6 +337,8 @@ def time_forward(t, torch, binding, reps, warm, flush=False):
         del scratch
         fms.sort()
         fl = fms[len(fms) // 2]
+    if graph:
+        return ms[len(ms) // 2], fl, graph_ms
     return ms[len(ms) // 2], fl
 
 
@@ -466,8 +494,12 @@ def other_workloads(torch, binding, synth, dev):
         w = synth.WORKLOADS[name]
         t = device_inputs(w, dev, torch)
         reps, warm = (5, 2) if name == "1m_steps" else (30, 20)
-        # the 130M-layer inputs (101 MB) fit the Infinity Cache: also timed after a flush
-        ms, fl = time_forward(t, torch, binding, reps, warm, flush=name == "130m_layer")
+        # the 130M-layer inputs (101 MB) fit the Infinity Cache: also timed after a flush; the
+        # short workloads also inside a replayed graph of 20 calls (kernel time without the
+        # host's per-call overhead, which the event pair around one call includes)
+        gr = 0 if name == "1m_steps" else 20
+        ms, fl, *gms = time_forward(t, torch, binding, reps, warm, flush=name == "130m_layer",
+                                    graph=gr)
         s = 2 if w.io_dtype == "bf16" else 4
         nbytes = scan_alg_bytes(w.batch, w.dim, w.seqlen, w.dstate, s, s)
         ws = binding.mamba_scan_workspace_bytes(w.batch, w.dim, w.seqlen, t["u"].dtype)
@@ -476,7 +508,9 @@ def other_workloads(torch, binding, synth, dev):
                          alg_GBps=nbytes / (ms * 1e-3) / 1e9,
                          alu_frac=w.channel_steps * ALU_OPS_PER_CHANNEL_STEP / (ms * 1e-3)
                          / ALU_PEAK_LANE_OPS,
-                         chunked=ws > 0)
+                         workspace_bytes=ws)
+        if gms:
+            res[name]["us_in_graph"] = gms[0] * 1e3
         if fl is not None:
             res[name]["us_mall_flushed"] = fl * 1e3
             res[name]["alg_GBps_mall_flushed"] = nbytes / (fl * 1e-3) / 1e9
