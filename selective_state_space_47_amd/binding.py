@@ -7,6 +7,7 @@ missing the first call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -50,6 +51,8 @@ def library_path() -> str:
 def lib():
     """The loaded native library (raises RuntimeError if it has not been built)."""
     global _LIB
+    if _LIB is not None:
+        return _LIB
     with _lock:
         if _LIB is None:
             path = library_path()
@@ -134,6 +137,11 @@ def _ptr(t):
 def _check(t, name, shape, dtype, device):
     if t is None:
         return
+    # fast path: one combined test for a well-formed tensor (the per-call host overhead matters
+    # for short sequences); anything else goes through the detailed checks below
+    if (type(t) is torch.Tensor and t.dtype is dtype and t.shape == shape
+            and t.get_device() == device.index and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != device:
@@ -144,6 +152,14 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+_NO_SWITCH = contextlib.nullcontext()
+
+
+def _on(dev):
+    """Context making `dev` current for a call; nothing to switch when it already is."""
+    return _NO_SWITCH if torch.cuda.current_device() == dev.index else torch.cuda.device(dev)
 
 
 def _raise(status):
@@ -200,7 +216,7 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     L_ = lib()
     ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = L_.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
@@ -238,7 +254,7 @@ def mamba_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         last_state = torch.empty((batch, dim, DSTATE), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (batch, dim, DSTATE), torch.float32, dev)
     dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = lib().mamba_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                                           _ptr(D), _ptr(z), _ptr(delta_bias),
@@ -290,7 +306,7 @@ def mamba_scan_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bi
     L_ = lib()
     ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = L_.mamba_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(width),
                                     _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -334,7 +350,7 @@ def mamba_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _check(out, "out", (batch, dim), io, dev)
     dm = make_dims(batch, dim, 1, code, DSTATE, 0)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = lib().mamba_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
                                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
@@ -399,7 +415,7 @@ def mamba_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     L_ = lib()
     ws_bytes = int(L_.mamba_scan_bwd_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev, min_bytes=1)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = L_.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dout),
@@ -431,7 +447,7 @@ def mamba_gemm_bf16(A, B, b_kcontig=True, c_trans=False, out=None):
     _check(out, "out", shape, torch.bfloat16, dev)
     ldb = K if b_kcontig else N
     ldc = M if c_trans else N
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = lib().mamba_gemm_bf16(_ptr(A), _ptr(B), _ptr(out), M, N, K, batch, K, ldb, N * K,
                                    ldc, M * N, int(bool(b_kcontig)), int(bool(c_trans)), stream)
@@ -485,7 +501,7 @@ def mamba_block_fwd(hidden, w_in, conv_weight, conv_bias, w_x, w_dt, dt_bias, A,
     L_ = lib()
     ws_bytes = int(L_.mamba_block_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev, min_bytes=1)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         st = L_.mamba_block_fwd(_ptr(hidden), _ptr(w_in), _ptr(conv_weight), _ptr(conv_bias),
                                 _ptr(w_x), _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D),
