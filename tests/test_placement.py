@@ -1,4 +1,5 @@
-"""The workgroup placement map of the scan kernels (host build of the header function, CPU)."""
+"""Host builds of header functions of the scan kernels (CPU): the workgroup placement map and the
+forward chunk plans."""
 import os
 import shutil
 import subprocess
@@ -22,3 +23,19 @@ def test_placement_map_is_a_contiguous_bijection(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0 and "bijective" in r.stdout, r.stdout + r.stderr
+
+
+def test_forward_plans(tmp_path):
+    """Kernel choice, chunk counts and workspace sizes of make_plan_fwd / make_plan for the five
+    workloads, the edges of the time-split rule, forced chunk lengths and a sweep of shapes."""
+    if not (shutil.which(HIPCC) or os.path.exists(HIPCC)):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "plan_check")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17",
+                        "-I", os.path.join(ROOT, "include"),
+                        "-I", os.path.join(ROOT, "selective_state_space_47_amd", "csrc"),
+                        "-o", exe, os.path.join(HERE, "host", "plan_check.hip")],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "plans:" in r.stdout, r.stdout + r.stderr
