@@ -11,9 +11,13 @@
 //  * The per-element rules are those of the whole-sequence forward in mamba_scan.hip.
 //
 // Why: the whole-sequence kernel gives each channel's recurrence to one group of 8 lanes for the
-// whole sequence.  With few channels (2 x 1536 of the 130M-layer shape, 1536 of the million-token
-// one) that leaves most SIMDs idle; splitting time across workgroups needs a separate summary
-// launch that repeats every exp.  Here the split is inside the workgroup instead:
+// whole sequence.  With few channels that leaves most SIMDs idle, and splitting time across
+// workgroups needs a separate summary launch that repeats every exp.  Here the split is inside
+// the workgroup instead.  The forward plan (make_plan_fwd) uses this kernel for grids of fewer
+// 4-channel blocks than CUs and sequences of at most 2048 tokens, where one launch beats two
+// (1 x 64 x 256 fp32: 15.3 -> 10.1 us per call).  For larger few-channel shapes (2 x 1536 x 2048,
+// long sequences) the chunked whole-sequence plan was measured faster: 4-channel workgroups share
+// the B/C staging 8 times less and meet three barriers per 16 tokens of each wave's work.
 //
 //  * A workgroup owns 4 channels of one sequence; each tile is 128 tokens = 8 segments of 16.
 //    Wave w takes segments 2w and 2w+1: lane = 16 c + 8 s + g handles channel c, segment 2w + s
