@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -55,11 +56,19 @@ CONV_OPS_PER_CHANNEL_STEP = ALU_OPS_PER_CHANNEL_STEP + 4 + 7
 FWD_KERNEL_SOURCES = ("mamba_common.h", "mamba_scan.hip")
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and with whitespace collapsed: an edit of a comment leaves
+    the kernel, and so the counters recorded for it, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(files=FWD_KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for name in files:
-        with open(os.path.join(ROOT, "selective_state_space_47_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "selective_state_space_47_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,6 @@
-// mamba_common.h -- device helpers, launch arguments and host-side validation shared by the
-// forward/step kernels (mamba_scan.hip) and the backward kernels (mamba_scan_bwd.hip).
+// mamba_common.h -- device helpers, launch arguments, launch plans and host-side validation
+// shared by the forward and step kernels (mamba_scan.hip), the time-split forward
+// (mamba_scan_ts.hip), the backward kernels (mamba_scan_bwd.hip) and the block's GEMMs.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

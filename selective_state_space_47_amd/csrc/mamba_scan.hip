@@ -18,13 +18,15 @@
 //  * Lane layout of the scan: a channel (b, d) is owned by 8 lanes; lane g holds states 2g and
 //    2g+1 in VGPRs.  A wave holds 8 channels, a workgroup 4 waves = 32 channels of one sequence.
 //    At 8 x 5120 channels this gives 5120 waves, i.e. exactly 5 per SIMD.
-//  * Per tile of 16 tokens: B and C are converted to fp32 once per workgroup and staged in LDS
+//  * Per 64-token tile: B and C are converted to fp32 once per workgroup and staged in LDS
 //    (shared by all 32 channels, read as a broadcast float4 per lane and token); u, Delta_raw
-//    and z are loaded by the owning wave, Delta = softplus(Delta_raw + bias) and Delta*u are
-//    computed once per (channel, token) and staged in LDS; each lane runs the sequential
-//    recurrence for its 2 states over the 16 tokens and writes its partial readout
-//    sum_{n in lane} C_n h_n to LDS; the epilogue adds the 8 partials, the skip and the gate,
-//    rounds to the output type and stores.
+//    and z are loaded by the owning wave one tile ahead.  Per 16-token sub-tile:
+//    Delta = softplus(Delta_raw + bias) and Delta*u are computed once per (channel, token) and
+//    staged in LDS; each lane runs the sequential recurrence for its 2 states over the 16 tokens
+//    and writes its partial readout sum_{n in lane} C_n h_n to LDS; the epilogue adds the 8
+//    partials, the skip and the gate, rounds to the output type and stores.
+//  * Small grids of short sequences use the time-split kernel of mamba_scan_ts.hip instead
+//    (make_plan_fwd chooses); the single-token state update (step_kernel) is at the end.
 //  * Long sequences are cut into chunks (grid dimension).  A first kernel writes, per channel
 //    and chunk, the chunk's local final state (from h = 0) and sum of Delta, i.e. the affine
 //    summary (prod Abar = exp(A * sum Delta), h_local).  The main kernel composes the summaries
