@@ -172,7 +172,8 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
  *   B, C             : (batch, dstate), io_dtype
  *   A, D, delta_bias : as for mamba_scan_fwd
  *
- * dims->seqlen must be 1 and dims->batch at most 65535 (MAMBA_ERR_SHAPE otherwise);
+ * dims->seqlen must be 1, dims->batch at most 65535 and dims->dim below 2^28 (MAMBA_ERR_SHAPE
+ * otherwise);
  * dims->chunk_len is ignored.  state and A must be 16-byte aligned.  NULL allowed for D, z,
  * delta_bias.
  */

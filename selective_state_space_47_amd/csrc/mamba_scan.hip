@@ -35,6 +35,7 @@
 #include <mutex>
 #include <type_traits>
 
+
 namespace mamba {
 
 // ------------------------------------------------------------------ scan
@@ -453,71 +454,142 @@ struct StepArgs {
   int32_t softplus;
 };
 
-// Four lanes per channel, four states per lane (one float4 of the state row each).  Each thread
-// serves kStepCh channels 64 apart, and every load of all of them is issued before any compute:
-// the step is bound by the state read and write, and with one 16-byte state load per thread the
-// memory system holds too few bytes in flight to reach HBM bandwidth.  A workgroup covers
-// 64 * kStepCh consecutive channels of one sequence.  Grid: (channel blocks, batch).
-constexpr int kStepCh = 2;
+// One token per sequence.  A wave covers 16 channels of kStepSeq sequences (a workgroup 64
+// channels of the same sequences), taken as groups of 4 sequences, and works in two lane layouts:
+//  * per (sequence, channel) pair, lane = 16 j + cp for sequence 4g + j of group g and channel
+//    dw + cp: u, Delta_raw, z, the bias and D are loaded (coalesced), Delta =
+//    softplus(Delta_raw + bias) and Delta*u are formed, and the epilogue (skip, gate, rounding,
+//    store) runs, once per pair;
+//  * per state quarter, lane = 4 c + q for channel dw + c and states 4q..4q+3: the state rows of
+//    the sequences are read and written as float4s (every wave instruction moves 1 KB of
+//    contiguous state), A is read once for all of them, and the recurrence and the partial
+//    readouts run.
+// Delta and Delta*u reach the quarter layout through ds_bpermute; the readout is summed over the
+// quad with DPP in a fixed order, and one more ds_bpermute per group hands each pair its sum.
+// The per-channel element-wise work and the addressing thus cost one wave instruction per 64
+// pairs instead of one per 16 (4 lanes of a channel repeating it), and each wave keeps
+// kStepSeq KB of state reads in flight: the step is bound by the state read and write.  The
+// arithmetic of Abar, Bbar*x and h is the whole-sequence scan's, so a decoded token continues a
+// scanned prefix exactly.  Grid: (ceil(dim / 64), ceil(batch / kStepSeq)).
+// Groups per workgroup, per step at 256 x 5120 (bf16, alternating builds in one process):
+// 1 group 32.4 us, 2 groups 29.6 us, 4 groups 32.5 us (114 VGPRs, 4 waves per SIMD).
+constexpr int kStepGroups = 2;
+constexpr int kStepSeq = 4 * kStepGroups;
 
 template <typename Tin>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
-  const int q = threadIdx.x & 3;
-  const int64_t d0 = (int64_t)blockIdx.x * (64 * kStepCh) + (threadIdx.x >> 2);
-  const int64_t b = blockIdx.y;
-  const Tin* U = static_cast<const Tin*>(p.u);
-  const Tin* DL = static_cast<const Tin*>(p.delta);
-  const Tin* Z = static_cast<const Tin*>(p.z);
-  const Tin* Bm = static_cast<const Tin*>(p.B);
-  const Tin* Cm = static_cast<const Tin*>(p.C);
-  const int64_t bo = b * kN + 4 * q;
-  float bb[4], cc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bb[i] = ld_f32(Bm, bo + i);
-    cc[i] = ld_f32(Cm, bo + i);
+  constexpr int kG = kStepGroups;
+  // B and C of the workgroup's sequences in fp32: [sequence][B 0..15, C 16..31]
+  __shared__ __align__(16) float sbc[kStepSeq][2 * kN];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in scalar registers
+  // Indices are 32-bit, so the clamps of uniform values stay scalar; the host keeps
+  // batch <= 65535 and dim < 2^28, so the largest lane byte offset, (3 dim + 15) * 4, is below
+  // 2^32.  Addressing: wave-uniform bases (scalar registers) plus 32-bit lane byte offsets.  The
+  // base channel is clamped like every lane's channel, so the offsets are small and non-negative
+  // even for a wave past the last channel (whose lanes store nothing).
+  const int nb = (int)p.batch, nd = (int)p.dim;
+  const int dw = (int)blockIdx.x * 64 + 16 * wv;  // the wave's first channel
+  const int dwb = min(dw, nd - 1);
+  const int b00 = (int)blockIdx.y * kStepSeq;     // the workgroup's first sequence
+
+  // ---- B, C of the sequences, converted once: thread t < 64 kG takes the pair 2t, 2t+1 of the
+  // values (sequence t / 16, row (t % 16) / 8 of B, C, states 2 (t % 8), +1)
+  if (tid < kStepSeq * kN) {
+    const int js = tid >> 4, r = (tid >> 3) & 1, n2 = 2 * (tid & 7);
+    const int bs = min(b00 + js, nb - 1);
+    const Tin* src = static_cast<const Tin*>(r ? p.C : p.B) + (int64_t)bs * kN + n2;
+    *reinterpret_cast<float2*>(&sbc[js][r * kN + n2]) = make_float2(ld_f32(src, 0), ld_f32(src, 1));
   }
-  float4 h[kStepCh], A4[kStepCh];
-  float x[kStepCh], dr[kStepCh], zz[kStepCh], bias[kStepCh], dsk[kStepCh];
-  bool ok[kStepCh];
+
+  // ---- pair layout: loads (clamped into range; out-of-range pairs store nothing); group g
+  // covers sequences b00 + 4g .. + 3
+  const int j = lane >> 4, cp = lane & 15;
+  const int cpo = min(dw + cp, nd - 1) - dwb;  // 0..15
+  const uint32_t opc = (uint32_t)cpo * 4u;     // byte offset from channel dwb (bias, D)
+  const float bias = p.bias ? *at(p.bias + dwb, opc) : 0.f;
+  const float dsk = p.D ? *at(p.D + dwb, opc) : 0.f;
+  float x[kG], draw[kG], zv[kG];
+  uint32_t op[kG];  // byte offsets from the group's base element (u, Delta_raw, z, out)
 #pragma unroll
-  for (int j = 0; j < kStepCh; ++j) {
-    const int64_t d = d0 + 64 * j;
-    ok[j] = d < p.dim;
-    const int64_t dc = ok[j] ? d : p.dim - 1;  // loads stay unconditional and in bounds
-    const int64_t ch = b * p.dim + dc;
-    h[j] = *(reinterpret_cast<const float4*>(p.state + ch * kN) + q);
-    A4[j] = *(reinterpret_cast<const float4*>(p.A + dc * kN) + q);
-    x[j] = ld_f32(U, ch);
-    dr[j] = ld_f32(DL, ch);
-    zz[j] = p.z ? ld_f32(Z, ch) : 0.f;
-    bias[j] = p.bias ? p.bias[dc] : 0.f;
-    dsk[j] = p.D ? p.D[dc] : 0.f;
+  for (int gi = 0; gi < kG; ++gi) {
+    const int b0 = b00 + 4 * gi;
+    const int64_t e0 = (int64_t)min(b0, nb - 1) * nd + dwb;
+    const int jo = min(b0 + j, nb - 1) - min(b0, nb - 1);  // 0..3
+    op[gi] = ((uint32_t)jo * (uint32_t)nd + (uint32_t)cpo) * (uint32_t)sizeof(Tin);
+    x[gi] = ld_f32(at(static_cast<const Tin*>(p.u) + e0, op[gi]), 0);
+    draw[gi] = ld_f32(at(static_cast<const Tin*>(p.delta) + e0, op[gi]), 0);
+    zv[gi] = p.z ? ld_f32(at(static_cast<const Tin*>(p.z) + e0, op[gi]), 0) : 0.f;
   }
+
+  // ---- quarter layout: loads
+  const int c = lane >> 2, q = lane & 3;
+  const bool okc = dw + c < nd;
+  // byte offset of the lane's float4 from the row of channel dwb (A, state)
+  const uint32_t oq = (uint32_t)((min(dw + c, nd - 1) - dwb) * kN + 4 * q) * 4u;
+  float4 a = *reinterpret_cast<const float4*>(at(p.A + (int64_t)dwb * kN, oq));
+  float4 h[kStepSeq];
 #pragma unroll
-  for (int j = 0; j < kStepCh; ++j) {
-    const int64_t d = d0 + 64 * j;
-    const int64_t ch = b * p.dim + d;
-    float dl = dr[j] + bias[j];
-    if (p.softplus) dl = softplus_f32(dl);
-    const float du = dl * x[j];
-    float4 hv = h[j];
-    hv.x = fmaf(fast_exp2(dl * A4[j].x * kLog2e), hv.x, du * bb[0]);
-    hv.y = fmaf(fast_exp2(dl * A4[j].y * kLog2e), hv.y, du * bb[1]);
-    hv.z = fmaf(fast_exp2(dl * A4[j].z * kLog2e), hv.z, du * bb[2]);
-    hv.w = fmaf(fast_exp2(dl * A4[j].w * kLog2e), hv.w, du * bb[3]);
-    float y = cc[0] * hv.x;
-    y = fmaf(cc[1], hv.y, y);
-    y = fmaf(cc[2], hv.z, y);
-    y = fmaf(cc[3], hv.w, y);
-    if (ok[j]) *(reinterpret_cast<float4*>(p.state + ch * kN) + q) = hv;
-    // sum the four partial readouts of the channel (fixed order)
-    y += __shfl_xor(y, 1);
-    y += __shfl_xor(y, 2);
-    if (q == 0 && ok[j]) {
-      y = fmaf(dsk[j], x[j], y);
-      if (p.z) y *= silu_f32(zz[j]);
-      st_out(static_cast<Tin*>(p.out), ch, y);
+  for (int jj = 0; jj < kStepSeq; ++jj) {
+    const int bs = min(b00 + jj, nb - 1);
+    h[jj] = *reinterpret_cast<const float4*>(at(p.state + ((int64_t)bs * nd + dwb) * kN, oq));
+  }
+
+  // ---- pair layout: Delta and Delta*u
+  float dl[kG], dx[kG];
+#pragma unroll
+  for (int gi = 0; gi < kG; ++gi) {
+    dl[gi] = draw[gi] + bias;
+    if (p.softplus) dl[gi] = softplus_f32(dl[gi]);
+    dx[gi] = dl[gi] * x[gi];
+  }
+  a.x *= kLog2e;
+  a.y *= kLog2e;
+  a.z *= kLog2e;
+  a.w *= kLog2e;
+  __syncthreads();  // sbc is written
+
+  // ---- quarter layout: the sequences in turn; lane 4c + q keeps the sum of sequence
+  // b00 + 4g + q in yq[g]
+  float yq[kG];
+#pragma unroll
+  for (int gi = 0; gi < kG; ++gi) yq[gi] = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < kStepSeq; ++jj) {
+    const int gi = jj >> 2, jq = jj & 3;
+    const int src = 4 * (16 * jq + c);  // byte address of the pair lane (b00 + jj, dw + c)
+    const float dlj = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dl[gi])));
+    const float dxj = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dx[gi])));
+    const float4 bb = *reinterpret_cast<const float4*>(&sbc[jj][4 * q]);
+    const float4 cc = *reinterpret_cast<const float4*>(&sbc[jj][kN + 4 * q]);
+    float4 hv = h[jj];
+    hv.x = fmaf(fast_exp2(dlj * a.x), hv.x, dxj * bb.x);
+    hv.y = fmaf(fast_exp2(dlj * a.y), hv.y, dxj * bb.y);
+    hv.z = fmaf(fast_exp2(dlj * a.z), hv.z, dxj * bb.z);
+    hv.w = fmaf(fast_exp2(dlj * a.w), hv.w, dxj * bb.w);
+    if (okc && b00 + jj < nb)
+      *reinterpret_cast<float4*>(at(p.state + ((int64_t)(b00 + jj) * nd + dwb) * kN, oq)) = hv;
+    float y = cc.x * hv.x;
+    y = fmaf(cc.y, hv.y, y);
+    y = fmaf(cc.z, hv.z, y);
+    y = fmaf(cc.w, hv.w, y);
+    // sum of the quad's four partial readouts (quad_perm xor 1, then xor 2; every lane of the
+    // quad ends with the same bits)
+    y += dpp_row<0xB1>(y);
+    y += dpp_row<0x4E>(y);
+    yq[gi] = q == jq ? y : yq[gi];
+  }
+
+  // ---- pair layout: lane 16 j + cp takes the sum of (b00 + 4g + j, dw + cp) from lane 4 cp + j
+#pragma unroll
+  for (int gi = 0; gi < kG; ++gi) {
+    float y =
+        __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * cp + j), __float_as_int(yq[gi])));
+    const int b0 = b00 + 4 * gi;
+    if (b0 + j < nb && dw + cp < nd) {
+      y = fmaf(dsk, x[gi], y);
+      if (p.z) y *= silu_f32(zv[gi]);
+      st_out(at(static_cast<Tin*>(p.out) + (int64_t)b0 * nd + dwb, op[gi]), 0, y);
     }
   }
 }
@@ -745,9 +817,10 @@ int mamba_state_update(float* state, const void* u, const void* delta, const flo
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
   a.bias = delta_bias; a.out = out; a.batch = dims->batch; a.dim = dims->dim;
   a.softplus = softplus_flag ? 1 : 0;
-  const int64_t xblocks = (dims->dim + 64 * kStepCh - 1) / (64 * kStepCh);
-  if (xblocks > 0x7fffffffLL || dims->batch > 65535) return MAMBA_ERR_SHAPE;
-  const dim3 grid((unsigned)xblocks, (unsigned)dims->batch);
+  const int64_t xblocks = (dims->dim + 63) / 64;
+  // the kernel's 32-bit lane byte offsets reach (3 * dim + 15) elements past a wave's base
+  if (dims->batch > 65535 || dims->dim >= (1LL << 28)) return MAMBA_ERR_SHAPE;
+  const dim3 grid((unsigned)xblocks, (unsigned)((dims->batch + kStepSeq - 1) / kStepSeq));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dims->io_dtype == MAMBA_BF16)
     hipLaunchKernelGGL((step_kernel<uint16_t>), grid, dim3(256), 0, s, a);

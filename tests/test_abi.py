@@ -144,6 +144,9 @@ def test_step_validation_codes(lib):
     assert step(dims(seqlen=1, dstate=32)) == -4
     assert step(dims(seqlen=1), state=ctypes.c_void_p(0x10004)) == -5   # state needs 16-B
     assert step(dims(seqlen=1, io=3)) == -3
+    assert step(dims(seqlen=1, batch=65536)) == -2
+    assert step(dims(seqlen=1, dim=1 << 28)) == -2   # 32-bit lane byte offsets of the kernel
+    assert step(dims(seqlen=1, batch=1, dim=(1 << 28) - 64), state=None) == -1  # shape accepted
 
 
 def call_bwd(lib, dm, u=FAKE, z=None, dz=None, dout=FAKE, du=FAKE, dB=FAKE, dA=FAKE, ws=FAKE,
