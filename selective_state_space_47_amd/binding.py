@@ -131,7 +131,37 @@ def mamba_scan_workspace_bytes(batch, dim, seqlen, io_dtype=torch.float32, dstat
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtypes convert it, which is cheaper than a c_void_p object
+    return None if t is None else t.data_ptr()
+
+
+# torch's own accessor of the current stream's raw handle (one C call); the public path builds a
+# Stream object per call, which costs more host time than a short scan's kernel
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(dev):
+    """Raw handle of the current stream on `dev`, as an int."""
+    if _raw_stream is not None:
+        return _raw_stream(dev.index)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+# dims structs (read-only for the library) and the forward's workspace size, per shape; short
+# sequences are called at a high rate with the same shape
+_FWD_CACHE = {}
+
+
+def _fwd_dims(batch, dim, L, code, chunk_len):
+    key = (batch, dim, L, code, chunk_len)
+    hit = _FWD_CACHE.get(key)
+    if hit is None:
+        dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+        hit = (dm, int(lib().mamba_scan_workspace_bytes(ctypes.byref(dm))))
+        if len(_FWD_CACHE) >= 1024:
+            _FWD_CACHE.clear()
+        _FWD_CACHE[key] = hit
+    return hit
 
 
 def _check(t, name, shape, dtype, device):
@@ -152,6 +182,17 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_group(tensors, shape, dtype, device):
+    """_check for several (tensor, name) pairs of one shape and dtype; the common case (all
+    well-formed) costs one Python call instead of one per tensor."""
+    idx = device.index
+    for t, name in tensors:
+        if t is not None and not (type(t) is torch.Tensor and t.dtype is dtype
+                                  and t.shape == shape and t.get_device() == idx
+                                  and t.is_contiguous()):
+            _check(t, name, shape, dtype, device)
 
 
 _NO_SWITCH = contextlib.nullcontext()
@@ -198,26 +239,20 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
         raise ValueError("tensors must be on a HIP device")
     io = u.dtype
     code = _io_code(io)
-    _check(u, "u", (batch, dim, L), io, dev)
-    _check(delta, "delta", (batch, dim, L), io, dev)
-    _check(z, "z", (batch, dim, L), io, dev)
-    _check(B, "B", (batch, DSTATE, L), io, dev)
-    _check(C, "C", (batch, DSTATE, L), io, dev)
-    _check(A, "A", (dim, DSTATE), torch.float32, dev)
-    _check(D, "D", (dim,), torch.float32, dev)
-    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     if out is None:
         out = torch.empty((batch, dim, L), dtype=io, device=dev)
-    _check(out, "out", (batch, dim, L), io, dev)
     if return_last_state and last_state is None:
         last_state = torch.empty((batch, dim, DSTATE), dtype=torch.float32, device=dev)
+    _check_group(((u, "u"), (delta, "delta"), (z, "z"), (out, "out")), (batch, dim, L), io, dev)
+    _check_group(((B, "B"), (C, "C")), (batch, DSTATE, L), io, dev)
+    _check(A, "A", (dim, DSTATE), torch.float32, dev)
+    _check_group(((D, "D"), (delta_bias, "delta_bias")), (dim,), torch.float32, dev)
     _check(last_state, "last_state", (batch, dim, DSTATE), torch.float32, dev)
-    dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+    dm, ws_bytes = _fwd_dims(batch, dim, L, code, chunk_len)
     L_ = lib()
-    ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev)
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = L_.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
                                _ptr(last_state), ctypes.byref(dm), _ptr(workspace), ws_len,
@@ -253,9 +288,9 @@ def mamba_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if return_last_state and last_state is None:
         last_state = torch.empty((batch, dim, DSTATE), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (batch, dim, DSTATE), torch.float32, dev)
-    dm = make_dims(batch, dim, L, code, DSTATE, chunk_len)
+    dm = _fwd_dims(batch, dim, L, code, chunk_len)[0]
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = lib().mamba_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                                           _ptr(D), _ptr(z), _ptr(delta_bias),
                                           int(bool(delta_softplus)), _ptr(out), _ptr(last_state),
@@ -307,7 +342,7 @@ def mamba_scan_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bi
     ws_bytes = int(L_.mamba_scan_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev)
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = L_.mamba_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(width),
                                     _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                     _ptr(delta_bias), int(bool(delta_softplus)), _ptr(out),
@@ -349,9 +384,9 @@ def mamba_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None
     if out is None:
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _check(out, "out", (batch, dim), io, dev)
-    dm = make_dims(batch, dim, 1, code, DSTATE, 0)
+    dm = _fwd_dims(batch, dim, 1, code, 0)[0]
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = lib().mamba_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
                                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                       int(bool(delta_softplus)), _ptr(out), ctypes.byref(dm),
@@ -416,7 +451,7 @@ def mamba_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     ws_bytes = int(L_.mamba_scan_bwd_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev, min_bytes=1)
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = L_.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(dout),
                                _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
@@ -448,7 +483,7 @@ def mamba_gemm_bf16(A, B, b_kcontig=True, c_trans=False, out=None):
     ldb = K if b_kcontig else N
     ldc = M if c_trans else N
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = lib().mamba_gemm_bf16(_ptr(A), _ptr(B), _ptr(out), M, N, K, batch, K, ldb, N * K,
                                    ldc, M * N, int(bool(b_kcontig)), int(bool(c_trans)), stream)
     _raise(st)
@@ -502,7 +537,7 @@ def mamba_block_fwd(hidden, w_in, conv_weight, conv_bias, w_x, w_dt, dt_bias, A,
     ws_bytes = int(L_.mamba_block_workspace_bytes(ctypes.byref(dm)))
     workspace, ws_len = _workspace(workspace, ws_bytes, dev, min_bytes=1)
     with _on(dev):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        stream = _stream(dev)
         st = L_.mamba_block_fwd(_ptr(hidden), _ptr(w_in), _ptr(conv_weight), _ptr(conv_bias),
                                 _ptr(w_x), _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D),
                                 _ptr(w_out), _ptr(out), ctypes.byref(dm), _ptr(workspace),

@@ -269,3 +269,25 @@ def test_binding_workspace_checks():
         binding._workspace(torch.empty(64, dtype=torch.uint8), 16, dev)      # host memory
     with pytest.raises(TypeError):
         binding._workspace(bytearray(64), 16, dev)
+
+
+def test_binding_tensor_checks():
+    """The binding's shape, dtype, layout and type checks (single and grouped) raise before
+    anything reaches the library; absent optional tensors pass."""
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.zeros((2, 3, 8))
+    binding._check(None, "z", (2, 3, 8), torch.float32, cpu)
+    binding._check(good, "u", (2, 3, 8), torch.float32, cpu)
+    binding._check_group(((good, "u"), (None, "z")), (2, 3, 8), torch.float32, cpu)
+    bad = [(torch.zeros((2, 3, 9)), ValueError),                  # shape
+           (torch.zeros((2, 3, 8), dtype=torch.bfloat16), ValueError),  # dtype
+           (torch.zeros((2, 8, 3)).transpose(1, 2), ValueError),  # not contiguous
+           (good.numpy(), TypeError)]                             # not a tensor
+    for t, err in bad:
+        with pytest.raises(err):
+            binding._check(t, "u", (2, 3, 8), torch.float32, cpu)
+        with pytest.raises(err):
+            binding._check_group(((good, "u"), (t, "delta")), (2, 3, 8), torch.float32, cpu)
+    with pytest.raises(ValueError):   # another device than the inputs'
+        binding._check_group(((good, "u"),), (2, 3, 8), torch.float32, torch.device("meta"))
