@@ -1,7 +1,8 @@
 // mamba_gemm.hip -- bf16 MFMA GEMMs for gfx950 (see mamba_gemm.h).
 //
 // gemm_big_kernel: both operands K-contiguous, 256 x 256 (or 256 x 128) workgroup tiles, one
-// wave per SIMD with 128 x 128 of accumulators, operands loaded straight into an LDS ring with
+// wave per SIMD with 128 x 128 of accumulators (two workgroups per CU with 256 x 128 tiles and a
+// shallower ring when K is short), operands loaded straight into an LDS ring with
 // global_load_lds_dwordx4.  gemm_kernel: everything else (N-contiguous B, small M or K), 128 x 128
 // tiles with register-staged loads.  Details at each kernel.
 // Operand layouts of v_mfma_f32_32x32x16_bf16 on gfx950 (checked with an in-bounds probe): lane l
@@ -436,8 +437,8 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
 
-template <int kTN, bool kSwap, int kBK, int kS>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs p) {
+template <int kTN, bool kSwap, int kBK, int kS, int kOcc>
+__global__ __launch_bounds__(256, kOcc) void gemm_big_kernel(GemmArgs p) {
   using S = BigShape<kTN, kBK, kS>;
   __shared__ uint4 smem[S::kSmem];
   const int lane = threadIdx.x & 63;
@@ -658,7 +659,7 @@ bool big_ok(const GemmArgs& a, bool b_kcontig) {
   return true;
 }
 
-template <int kTN, int kBK, int kS>
+template <int kTN, int kBK, int kS, int kOcc = 1>
 int launch_big(const GemmArgs& a0, int64_t batch, hipStream_t s) {
   using S = BigShape<kTN, kBK, kS>;
   GemmArgs a = a0;
@@ -669,9 +670,9 @@ int launch_big(const GemmArgs& a0, int64_t batch, hipStream_t s) {
     return MAMBA_ERR_SHAPE;
   const dim3 grid((unsigned)((int64_t)a.mtiles * a.ntiles * batch));
   if (a.dst[0].trans)
-    hipLaunchKernelGGL((gemm_big_kernel<kTN, false, kBK, kS>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_big_kernel<kTN, false, kBK, kS, kOcc>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_big_kernel<kTN, true, kBK, kS>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_big_kernel<kTN, true, kBK, kS, kOcc>), grid, dim3(256), 0, s, a);
   return launch_status();
 }
 
@@ -712,6 +713,11 @@ int launch_gemm(const GemmArgs& a, bool b_kcontig, int64_t batch, hipStream_t s)
     // A 256-wide tile costs about 1.6 times a 128-wide one (in_proj in whole rounds: 737 against
     // 918 us) while moving fewer bytes per flop; take it unless its rounds cost more.  out_proj
     // (640 or 1280 tiles) runs 390 us with 256-wide tiles against 440 us with 128-wide ones.
+    // Short K (at most 8 steps): the time is mostly the epilogue's stores, so 256 x 128 tiles with
+    // a 3-stage ring (72 KB of LDS, 198 VGPRs), two workgroups per CU, let one workgroup's stores
+    // overlap the other's MFMAs: dt_proj (K = 160) 59.6 -> 48.2 us.  With long K the larger tile
+    // wins (in_proj 713 against 818 us, out_proj 379 against 395 us).
+    if (a.K <= 8 * kBigBK) return launch_big<128, kBigBK, 3, 2>(a, batch, s);
     if (16 * tile_rounds(t256) <= 10 * tile_rounds(t128))
       return launch_big<256, kBigBK, kBigStages>(a, batch, s);
     return launch_big<128, kBigBK, kBigStages>(a, batch, s);
