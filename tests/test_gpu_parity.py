@@ -411,6 +411,36 @@ def test_state_update_edge(io, batch, dim):
     assert rel_err(state.cpu().numpy(), rs) <= 1e-4
 
 
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,dim", [(9, 17), (13, 65), (5, 200), (16, 64)])
+@pytest.mark.parametrize("optional", [True, False], ids=["all_inputs", "no_D_z_bias"])
+def test_state_update_ragged(io, batch, dim, optional):
+    """The step kernel serves 64 channels of 8 sequences per workgroup in groups of 4 sequences:
+    partial groups (9, 13 and 5 sequences), waves past the last channel (17, 65 and 200
+    channels) and an exact tile (16 x 64); with and without D, z, the bias and softplus.  Every
+    output and state is compared with the oracle; a canary row after the state is untouched."""
+    rng = np.random.default_rng(batch * 1000 + dim)
+    st0 = rng.standard_normal((batch, dim, 16)).astype(np.float32)
+    w = synth.random_case(7, batch, dim, 1, bf16=io == torch.bfloat16)
+    u, dl, z = (w[k][:, :, 0] for k in ("u", "delta", "z"))
+    B, C = w["B"][:, :, 0], w["C"][:, :, 0]
+    D, bias = (w["D"], w["delta_bias"]) if optional else (None, None)
+    zz = z if optional else None
+    print(f"[step ragged] io={io} batch={batch} dim={dim} optional={optional}", flush=True)
+    buf = dev(np.concatenate([st0.reshape(-1), np.full(64, 7.0, np.float32)]))
+    state = buf[: batch * dim * 16].view(batch, dim, 16)
+    y = binding.mamba_state_update(state, dev(u, io), dev(dl, io), dev(w["A"]), dev(B, io),
+                                   dev(C, io), None if D is None else dev(D),
+                                   None if zz is None else dev(zz, io),
+                                   None if bias is None else dev(bias), optional)
+    torch.cuda.synchronize()
+    ry, rs = oracle.state_update_ref(st0, u, dl, w["A"], B, C, D, zz, bias, optional)
+    tol = 1e-2 if io == torch.bfloat16 else 1e-4
+    assert rel_err(y.float().cpu().numpy(), ry) <= tol
+    assert rel_err(state.cpu().numpy(), rs) <= 1e-4
+    assert bool((buf[batch * dim * 16:] == 7.0).all())
+
+
 def test_bf16_output_rounding_is_nearest_even():
     """With z off and D = 1, u = 0: out is the fp32 readout rounded once to bf16; compare with
     the fp32 path rounded on the host (nearest, ties to even)."""
