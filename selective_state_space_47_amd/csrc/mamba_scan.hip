@@ -475,6 +475,7 @@ struct StepArgs {
 // 1 group 32.4 us, 2 groups 29.6 us, 4 groups 32.5 us (114 VGPRs, 4 waves per SIMD).
 constexpr int kStepGroups = 2;
 constexpr int kStepSeq = 4 * kStepGroups;
+static_assert(kStepSeq * kN <= 256, "one staging thread per B/C value pair of the workgroup");
 
 template <typename Tin>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
@@ -493,8 +494,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p) {
   const int dwb = min(dw, nd - 1);
   const int b00 = (int)blockIdx.y * kStepSeq;     // the workgroup's first sequence
 
-  // ---- B, C of the sequences, converted once: thread t < 64 kG takes the pair 2t, 2t+1 of the
-  // values (sequence t / 16, row (t % 16) / 8 of B, C, states 2 (t % 8), +1)
+  // ---- B, C of the sequences, converted once: thread t < 16 kStepSeq takes the pair 2t, 2t+1
+  // of the values (sequence t / 16, row (t % 16) / 8 of B, C, states 2 (t % 8), +1)
   if (tid < kStepSeq * kN) {
     const int js = tid >> 4, r = (tid >> 3) & 1, n2 = 2 * (tid & 7);
     const int bs = min(b00 + js, nb - 1);
